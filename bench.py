@@ -1,0 +1,146 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE expert FFN hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload tp_slice]
+
+One step = the whole hot path on one batch of synthetic input already resident
+in HBM: routing tables (moe_plan), grouped Linear1 with the fused
+SwiGLU/requant epilogue, grouped Linear2, and the top-k combine, enqueued on
+one stream.  The four stages are the same calls moe_forward makes; they are
+issued one by one so HIP events on that stream can time each kernel.  Three
+copies of the expert weights are rotated between steps so they stream from
+HBM rather than the 256 MB Infinity Cache.
+
+Prints one JSON line with the metric (useful TFLOP/s = 2 * N_valid * 3 * H * I
+per step, the reading notes' FLOP count), tokens/s, the roofline of the
+dominant kernel measured with HIP events, and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer useful TFLOP/s + tokens/s at 1 GPU; % of scaled-MFMA peak / HBM BW"
+PEAK_MFMA_TFLOPS = 5000.0      # MI355X dense FP8 MFMA; FP8 x FP4 scaled MFMA issues at this rate
+PEAK_HBM_GBS = 8000.0
+
+
+def cpu_baseline(w, d_gpu, sample_tokens: int):
+    """Time the CPU oracle (untuned) on the first `sample_tokens` tokens of the workload."""
+    import numpy as np
+    from moe_expert_ffn_plan_amd import inputs
+    from oracle.forward import forward_tokens
+    d = inputs.to_numpy(d_gpu)
+    toks = np.arange(min(sample_tokens, w.num_tokens))
+    t0 = time.perf_counter()
+    _, hits = forward_tokens(toks, d["x"], d["x_sf"], d["topk_idx"], d["topk_w"], d["w1"], d["w1_sf"], d["w2"],
+                             d["w2_sf"], num_experts=w.num_experts, expert_begin=0)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * len(hits) * 3 * w.hidden * w.intermediate
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) or 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {toks.size} tokens ({len(hits)} local top-k rows), whole oracle forward incl. "
+                      f"weight dequantisation, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="tp_slice")
+    ap.add_argument("--weight-copies", type=int, default=3)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=384)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs one GPU's share of the MoE layer; --gpus {args.gpus} is not supported "
+              f"(the multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        return 2
+
+    import torch
+    from moe_expert_ffn_plan_amd import binding as B
+    from moe_expert_ffn_plan_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS[args.workload]
+    s = B.shape_of(w)
+    d = inputs.make_inputs(w, device=dev)
+    weights = [{k: d[k] for k in ("w1", "w1_sf", "w2", "w2_sf")}]
+    for c in range(1, args.weight_copies):
+        weights.append(inputs.make_weights(w, device=dev, weight_seed=w.weight_seed + 1000 * c))
+    plan_ws = torch.empty(B.plan_workspace_bytes(s), dtype=torch.uint8, device=dev)
+    ws = torch.empty(B.forward_workspace_bytes(s), dtype=torch.uint8, device=dev)
+    y = torch.empty(w.num_tokens, w.hidden, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    stages = ["plan", "linear1", "linear2", "combine"]
+
+    def step(i, events=None):
+        wt = weights[i % len(weights)]
+        rec = (lambda j: events[j].record(stream)) if events is not None else (lambda j: None)
+        rec(0)
+        B.plan(s, d["topk_idx"], plan_ws, stream)
+        rec(1)
+        B.linear1(s, d["x"], d["x_sf"], d["topk_w"], wt["w1"], wt["w1_sf"], plan_ws, ws, stream)
+        rec(2)
+        B.linear2(s, wt["w2"], wt["w2_sf"], plan_ws, ws, stream)
+        rec(3)
+        B.combine(s, plan_ws, ws, y, stream)
+        rec(4)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    scal = B.plan_view(s, plan_ws)["scalars"].cpu().tolist()
+    r_pad, n_valid = scal[0], scal[2]
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    kern_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, name in enumerate(stages)}
+
+    H, I = w.hidden, w.intermediate
+    useful = 2.0 * n_valid * 3 * H * I
+    tflops = useful / (ms * 1e-3) / 1e12
+    l1_flops = 2.0 * n_valid * 2 * I * H
+    l1_tflops = l1_flops / (kern_ms["linear1"] * 1e-3) / 1e12
+    roofline = {"kernel": "linear1 (gemm_kernel<BM, true>)", "bound": "mfma", "achieved": round(l1_tflops, 2),
+                "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(l1_tflops / PEAK_MFMA_TFLOPS, 4),
+                "traffic": None}
+    out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "fp8e4m3 x fp4e2m1 (fp32 accumulate)", "data": "synthetic",
+           "config": {"workload": w.name, "tokens": w.num_tokens, "hidden": H, "intermediate": I,
+                      "local_experts": w.num_experts, "topk": w.topk, "block_m": w.block_m,
+                      "valid_rows": n_valid, "padded_rows": r_pad, "weight_copies": args.weight_copies},
+           "tokens_per_s": round(w.num_tokens / (ms * 1e-3), 1),
+           "pct_of_mfma_peak": round(100 * tflops / PEAK_MFMA_TFLOPS, 2),
+           "kernel_ms": {k: round(v, 4) for k, v in kern_ms.items()},
+           "roofline": roofline}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, {k: v for k, v in d.items()}, args.cpu_sample_tokens)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

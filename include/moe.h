@@ -1,0 +1,211 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) fused MoE expert FFN library
+ * (libmoe_mi355x.so).
+ *
+ * One GPU's share of a mixture-of-experts FFN forward, as described by the
+ * DeepGEMM "MegaMoE" pages and the fused-MoE practice page:
+ *   routing tables -> grouped Linear1 (FP8 E4M3 activations x FP4 E2M1
+ *   weights, UE8M0 per-32 scales) -> SwiGLU x top-k weight -> FP8 requant
+ *   -> grouped Linear2 -> FP32 top-k combine written as BF16.
+ *
+ * Conventions for every entry point:
+ *  - Tensor arguments are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or keeps them.  Row-major, contiguous.
+ *  - Pointers must be 16-byte aligned (topk_idx 8, topk_w 4); the workspace
+ *    pointers 256-byte aligned.  Otherwise MOE_ERR_ALIGN.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    outputs are valid once the stream reaches the call.  No call blocks on
+ *    the GPU.  Calls that share a workspace must not overlap in time.
+ *  - Validation happens on the host before anything is enqueued, in this
+ *    order: NULL shape/pointers (MOE_ERR_NULL), shape limits (MOE_ERR_SHAPE),
+ *    alignment (MOE_ERR_ALIGN), workspace size (MOE_ERR_WORKSPACE), device
+ *    architecture (MOE_ERR_ARCH).  A failed kernel launch returns
+ *    MOE_ERR_HIP.  num_tokens == 0 is a no-op returning MOE_OK.
+ *  - Expert ids outside [expert_begin, expert_begin + num_experts) are not
+ *    errors: those top-k entries are simply not computed on this GPU (the
+ *    pages' "valid expert" test).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,
+    MOE_ERR_SHAPE = -2,
+    MOE_ERR_ALIGN = -3,
+    MOE_ERR_WORKSPACE = -4,
+    MOE_ERR_ARCH = -5,
+    MOE_ERR_HIP = -6
+};
+
+/* Problem shape.  Limits (else MOE_ERR_SHAPE, or MOE_ERR_ALIGN for the
+ * divisibility rules):
+ *   num_tokens   T >= 0, T * topk < 2^30
+ *   hidden       H > 0, multiple of 256 (Linear1 K-steps of 128 and
+ *                Linear2 output tiles of 256 columns)
+ *   intermediate I > 0, multiple of 128 (Linear1 emits 2I interleaved
+ *                gate/up columns in tiles of 256; Linear2 K-steps of 128)
+ *   num_experts  E local experts, 1..512
+ *   expert_begin global id of local expert 0
+ *   topk         k, 1..64
+ *   block_m      rows per routing block, one of 16, 32, 64, 128; each
+ *                expert's rows are padded to a multiple of it.
+ */
+typedef struct moe_shape {
+    int32_t num_tokens;
+    int32_t hidden;
+    int32_t intermediate;
+    int32_t num_experts;
+    int32_t expert_begin;
+    int32_t topk;
+    int32_t block_m;
+} moe_shape;
+
+/* Worst-case padded row count of the routing layout ("pool capacity"):
+ * align(T * k + E * (block_m - 1), block_m).  This is the SymmBuffer page's
+ * pool formula (section 6.2) for one rank, with k in place of min(k, E) so
+ * that a token that names one expert twice stays in bounds; the two agree
+ * for k <= E.  Returns MOE_OK and writes *rows, or an error status. */
+MOE_API int moe_capacity_rows(const moe_shape* shape, int64_t* rows);
+
+/* ---- routing tables ------------------------------------------------------
+ * What is built follows the practice page's schedule tables (section 2) and
+ * the MegaMoE dispatch counting (walk-through section 4.2, steps 1 and 3):
+ * per-expert hit counts, each expert's row range padded to block_m, a slot
+ * for every valid top-k entry (rows of one expert in ascending t*k+j
+ * order), the inverse tables, per-block expert id and padding slack, and the
+ * pull order (tokens with a hit, ascending by their smallest slot).
+ * The tables are bit-identical for identical inputs. */
+
+/* Bytes of the plan workspace for this shape. */
+MOE_API int moe_plan_workspace_bytes(const moe_shape* shape, size_t* bytes);
+
+/* Build the routing tables of topk_idx (int64 [T, k], global expert ids)
+ * into plan_ws (>= moe_plan_workspace_bytes, 256-byte aligned).  One kernel
+ * launch; nothing to initialise beforehand. */
+MOE_API int moe_plan(const moe_shape* shape, const int64_t* topk_idx,
+             void* plan_ws, size_t plan_ws_bytes, void* stream);
+
+/* Device pointers to the tables inside a plan workspace (no GPU work).
+ *   scalars[4]      int32: R_pad (padded rows used), n_pull, N (valid hits),
+ *                   n_blocks (= R_pad / block_m)
+ *   counts[E]       hits per local expert
+ *   offsets[E+1]    first padded row of each expert; offsets[E] = R_pad
+ *   slot[T*k]       row of top-k entry (t, j), -1 if not local
+ *   row_token[cap]  token of each row, -1 for padding (rows < R_pad)
+ *   row_topk[cap]   top-k index j of each row, -1 for padding (rows < R_pad)
+ *   block_expert[cap/block_m]  local expert of each block (blocks < n_blocks)
+ *   slack[cap/block_m]         padding rows of each block (blocks < n_blocks)
+ *   pull_order[T]   tokens with >= 1 local hit by smallest slot (first n_pull)
+ * Entries past the stated ranges are unspecified. */
+typedef struct moe_plan_view {
+    int32_t* scalars;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* slot;
+    int32_t* row_token;
+    int32_t* row_topk;
+    int32_t* block_expert;
+    int32_t* slack;
+    int32_t* pull_order;
+    int64_t capacity_rows;
+} moe_plan_view;
+MOE_API int moe_plan_view_get(const moe_shape* shape, void* plan_ws, moe_plan_view* out);
+
+/* ---- forward ---------------------------------------------------------------
+ * Inputs (formats of the reading notes' "numerical formats" table):
+ *   x        uint8 [T, H]        FP8 E4M3 (OCP, max 448)
+ *   x_sf     uint8 [T, H/32]     UE8M0 scale of each 32 consecutive x values
+ *   topk_idx int64 [T, k]        global expert ids
+ *   topk_w   float [T, k]        routing weights (applied in the Linear1
+ *                                epilogue, walk-through section 4.6)
+ *   w1       uint8 [E, 2I, H/2]  FP4 E2M1 pairs, even K in the low nibble;
+ *                                rows interleave gate/up by 8:
+ *                                [g0..7, u0..7, g8..15, u8..15, ...]
+ *                                (walk-through section 7.3)
+ *   w1_sf    uint8 [E, 2I, H/32] UE8M0, one per row per 32 K
+ *   w2       uint8 [E, H, I/2]   FP4 E2M1 pairs
+ *   w2_sf    uint8 [E, H, I/32]  UE8M0
+ * Output:
+ *   y        uint16 [T, H]       BF16; y[t] = sum over t's local top-k
+ *                                entries (j ascending, FP32) of the BF16
+ *                                Linear2 rows; +0 for a token with none.
+ * plan_ws: tables built by moe_plan for the same topk_idx and shape, or
+ *   NULL to build them inside ws as part of this call.
+ * ws: workspace of >= moe_forward_workspace_bytes, 256-byte aligned; holds
+ *   the FP8 Linear2 input (and its scales) and the BF16 per-slot Linear2
+ *   rows between kernels. */
+MOE_API int moe_forward_workspace_bytes(const moe_shape* shape, size_t* bytes);
+MOE_API int moe_forward(const moe_shape* shape,
+                const uint8_t* x, const uint8_t* x_sf,
+                const int64_t* topk_idx, const float* topk_w,
+                const uint8_t* w1, const uint8_t* w1_sf,
+                const uint8_t* w2, const uint8_t* w2_sf,
+                uint16_t* y,
+                const void* plan_ws,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* ---- the forward's stages, one kernel each ---------------------------------
+ * moe_forward(plan_ws != NULL) is exactly moe_linear1, moe_linear2 and
+ * moe_combine in this order on one stream; they are exposed so a caller can
+ * schedule or time the stages itself.  Arguments mean what they mean for
+ * moe_forward; plan_ws (from moe_plan) is required here, and ws must be the
+ * same forward workspace for all three.
+ *   moe_linear1: grouped Linear1 over the routing layout with the fused
+ *     SwiGLU x top-k weight and FP8 requant epilogue -> h_q, h_sf in ws
+ *     (reading notes "stage three" and "stage four").
+ *   moe_linear2: grouped Linear2 of h_q with BF16 output -> yslot in ws
+ *     ("stage five").
+ *   moe_combine: y[t] = BF16(FP32 sum over j of yslot[slot[t, j]])
+ *     ("stage six"; walk-through section 4.6 "combine reduction"). */
+MOE_API int moe_linear1(const moe_shape* shape,
+                const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
+                const uint8_t* w1, const uint8_t* w1_sf,
+                const void* plan_ws, void* ws, size_t ws_bytes, void* stream);
+MOE_API int moe_linear2(const moe_shape* shape,
+                const uint8_t* w2, const uint8_t* w2_sf,
+                const void* plan_ws, void* ws, size_t ws_bytes, void* stream);
+MOE_API int moe_combine(const moe_shape* shape, const void* plan_ws,
+                const void* ws, size_t ws_bytes, uint16_t* y, void* stream);
+
+/* Device pointers to the intermediates inside a forward workspace, for
+ * tests (no GPU work):
+ *   h_q   uint8  [cap, I]     FP8 E4M3 Linear2 input (SwiGLU x w, requantised)
+ *   h_sf  uint8  [cap, I/32]  its UE8M0 scales
+ *   yslot uint16 [cap, H]     BF16 Linear2 output per slot row
+ *   plan  the plan region used when moe_forward got plan_ws == NULL
+ * Rows of padding (and rows >= R_pad) hold unspecified values. */
+typedef struct moe_forward_view {
+    uint8_t* h_q;
+    uint8_t* h_sf;
+    uint16_t* yslot;
+    void* plan;
+    int64_t capacity_rows;
+} moe_forward_view;
+MOE_API int moe_forward_view_get(const moe_shape* shape, void* ws, moe_forward_view* out);
+
+/* MOE_OK if `device` is a gfx950 GPU, MOE_ERR_ARCH if not, MOE_ERR_HIP if
+ * the runtime cannot be queried. */
+MOE_API int moe_device_supported(int device);
+
+/* Static string naming a status code. */
+MOE_API const char* moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,226 @@
+// C ABI of the fused MoE expert FFN library: host-side validation,
+// workspace carving and the kernel sequence
+//   routing -> Linear1 (+SwiGLU/requant) -> Linear2 (+BF16) -> combine,
+// all enqueued on the caller's stream.  Interface modelled on the pages'
+// host API: a size query plus caller-owned buffer (SymmBuffer page,
+// sections 5-6), one forward entry point with strict shape checks that
+// answer "unsupported" (reading notes, "host-side checks").
+#include <atomic>
+#include <cstring>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other architecture
+std::atomic<int> g_arch_cache[kMaxDevices];
+
+int check_arch_current() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    return moe_device_supported(dev);
+}
+
+int check_shape(const moe_shape* s) {
+    if (!s) return MOE_ERR_NULL;
+    if (s->num_tokens < 0 || s->hidden <= 0 || s->intermediate <= 0) return MOE_ERR_SHAPE;
+    if (s->num_experts < 1 || s->num_experts > kMaxExperts) return MOE_ERR_SHAPE;
+    if (s->topk < 1 || s->topk > kMaxTopk) return MOE_ERR_SHAPE;
+    if (!(s->block_m == 16 || s->block_m == 32 || s->block_m == 64 || s->block_m == 128)) return MOE_ERR_SHAPE;
+    if ((int64_t)s->num_tokens * s->topk >= (1ll << 30)) return MOE_ERR_SHAPE;
+    if (s->hidden > (1 << 20) || s->intermediate > (1 << 20)) return MOE_ERR_SHAPE;
+    if (s->hidden % 256 != 0 || s->intermediate % 128 != 0) return MOE_ERR_ALIGN;
+    // kernels address each operand's rows with 32-bit offsets
+    const int64_t lim = 1ll << 31;
+    if ((int64_t)s->num_tokens * s->hidden >= lim) return MOE_ERR_SHAPE;
+    if (capacity_rows(*s) * s->intermediate >= lim) return MOE_ERR_SHAPE;
+    if ((int64_t)s->hidden * s->intermediate >= lim) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_device_supported(int device) {
+    if (device < 0) return MOE_ERR_HIP;
+    if (device < kMaxDevices) {
+        const int c = g_arch_cache[device].load(std::memory_order_relaxed);
+        if (c == 1) return MOE_OK;
+        if (c == 2) return MOE_ERR_ARCH;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return MOE_ERR_HIP;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (device < kMaxDevices) g_arch_cache[device].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? MOE_OK : MOE_ERR_ARCH;
+}
+
+const char* moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "null pointer";
+        case MOE_ERR_SHAPE: return "unsupported shape";
+        case MOE_ERR_ALIGN: return "misaligned pointer or dimension";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_ARCH: return "device is not gfx950";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int moe_capacity_rows(const moe_shape* shape, int64_t* rows) {
+    if (!rows) return MOE_ERR_NULL;
+    const int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    *rows = capacity_rows(*shape);
+    return MOE_OK;
+}
+
+int moe_plan_workspace_bytes(const moe_shape* shape, size_t* bytes) {
+    if (!bytes) return MOE_ERR_NULL;
+    const int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    *bytes = plan_layout(*shape).total;
+    return MOE_OK;
+}
+
+int moe_forward_workspace_bytes(const moe_shape* shape, size_t* bytes) {
+    if (!bytes) return MOE_ERR_NULL;
+    const int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    *bytes = forward_layout(*shape).total;
+    return MOE_OK;
+}
+
+int moe_plan_view_get(const moe_shape* shape, void* plan_ws, moe_plan_view* out) {
+    if (!out || !plan_ws) return MOE_ERR_NULL;
+    const int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const PlanLayout L = plan_layout(*shape);
+    const PlanPtrs p = plan_ptrs(L, plan_ws);
+    out->scalars = p.scalars; out->counts = p.counts; out->offsets = p.offsets; out->slot = p.slot;
+    out->row_token = p.row_token; out->row_topk = p.row_topk; out->block_expert = p.block_expert;
+    out->slack = p.slack; out->pull_order = p.pull_order; out->capacity_rows = L.cap;
+    return MOE_OK;
+}
+
+int moe_forward_view_get(const moe_shape* shape, void* ws, moe_forward_view* out) {
+    if (!out || !ws) return MOE_ERR_NULL;
+    const int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const ForwardLayout F = forward_layout(*shape);
+    char* b = static_cast<char*>(ws);
+    out->h_q = reinterpret_cast<uint8_t*>(b + F.h_q);
+    out->h_sf = reinterpret_cast<uint8_t*>(b + F.h_sf);
+    out->yslot = reinterpret_cast<uint16_t*>(b + F.yslot);
+    out->plan = b + F.plan_base;
+    out->capacity_rows = F.plan.cap;
+    return MOE_OK;
+}
+
+int moe_plan(const moe_shape* shape, const int64_t* topk_idx, void* plan_ws, size_t plan_ws_bytes,
+             void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->num_tokens == 0) return MOE_OK;
+    if (!topk_idx || !plan_ws) return MOE_ERR_NULL;
+    if (!aligned(topk_idx, 8) || !aligned(plan_ws, kAlign)) return MOE_ERR_ALIGN;
+    const PlanLayout L = plan_layout(*shape);
+    if (plan_ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if ((st = check_arch_current()) != MOE_OK) return st;
+    const hipError_t e = launch_route(*shape, topk_idx, plan_ptrs(L, plan_ws), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_linear1(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
+                const uint8_t* w1, const uint8_t* w1_sf, const void* plan_ws, void* ws, size_t ws_bytes,
+                void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->num_tokens == 0) return MOE_OK;
+    if (!x || !x_sf || !topk_w || !w1 || !w1_sf || !plan_ws || !ws) return MOE_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(x_sf, 16) || !aligned(w1, 16) || !aligned(w1_sf, 16) || !aligned(topk_w, 4) ||
+        !aligned(ws, kAlign) || !aligned(plan_ws, kAlign))
+        return MOE_ERR_ALIGN;
+    const ForwardLayout F = forward_layout(*shape);
+    if (ws_bytes < F.total) return MOE_ERR_WORKSPACE;
+    if ((st = check_arch_current()) != MOE_OK) return st;
+    const PlanPtrs p = plan_ptrs(F.plan, const_cast<void*>(plan_ws));
+    char* base = static_cast<char*>(ws);
+    const GemmProblem g{shape, &p, F.plan.cap};
+    const hipError_t e = launch_linear1(g, x, x_sf, topk_w, w1, w1_sf, reinterpret_cast<uint8_t*>(base + F.h_q),
+                                        reinterpret_cast<uint8_t*>(base + F.h_sf), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_linear2(const moe_shape* shape, const uint8_t* w2, const uint8_t* w2_sf, const void* plan_ws, void* ws,
+                size_t ws_bytes, void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->num_tokens == 0) return MOE_OK;
+    if (!w2 || !w2_sf || !plan_ws || !ws) return MOE_ERR_NULL;
+    if (!aligned(w2, 16) || !aligned(w2_sf, 16) || !aligned(ws, kAlign) || !aligned(plan_ws, kAlign))
+        return MOE_ERR_ALIGN;
+    const ForwardLayout F = forward_layout(*shape);
+    if (ws_bytes < F.total) return MOE_ERR_WORKSPACE;
+    if ((st = check_arch_current()) != MOE_OK) return st;
+    const PlanPtrs p = plan_ptrs(F.plan, const_cast<void*>(plan_ws));
+    char* base = static_cast<char*>(ws);
+    const GemmProblem g{shape, &p, F.plan.cap};
+    const hipError_t e = launch_linear2(g, reinterpret_cast<uint8_t*>(base + F.h_q),
+                                        reinterpret_cast<uint8_t*>(base + F.h_sf), w2, w2_sf,
+                                        reinterpret_cast<uint16_t*>(base + F.yslot), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_combine(const moe_shape* shape, const void* plan_ws, const void* ws, size_t ws_bytes, uint16_t* y,
+                void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->num_tokens == 0) return MOE_OK;
+    if (!plan_ws || !ws || !y) return MOE_ERR_NULL;
+    if (!aligned(y, 16) || !aligned(ws, kAlign) || !aligned(plan_ws, kAlign)) return MOE_ERR_ALIGN;
+    const ForwardLayout F = forward_layout(*shape);
+    if (ws_bytes < F.total) return MOE_ERR_WORKSPACE;
+    if ((st = check_arch_current()) != MOE_OK) return st;
+    const PlanPtrs p = plan_ptrs(F.plan, const_cast<void*>(plan_ws));
+    const char* base = static_cast<const char*>(ws);
+    const hipError_t e = launch_combine(*shape, reinterpret_cast<const uint16_t*>(base + F.yslot), p.slot, y,
+                                        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_forward(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, const int64_t* topk_idx,
+                const float* topk_w, const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2,
+                const uint8_t* w2_sf, uint16_t* y, const void* plan_ws, void* ws, size_t ws_bytes,
+                void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->num_tokens == 0) return MOE_OK;
+    if (!x || !x_sf || !topk_idx || !topk_w || !w1 || !w1_sf || !w2 || !w2_sf || !y || !ws) return MOE_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(x_sf, 16) || !aligned(w1, 16) || !aligned(w1_sf, 16) || !aligned(w2, 16) ||
+        !aligned(w2_sf, 16) || !aligned(y, 16) || !aligned(topk_idx, 8) || !aligned(topk_w, 4) ||
+        !aligned(ws, kAlign) || (plan_ws && !aligned(plan_ws, kAlign)))
+        return MOE_ERR_ALIGN;
+    const ForwardLayout F = forward_layout(*shape);
+    if (ws_bytes < F.total) return MOE_ERR_WORKSPACE;
+    if ((st = check_arch_current()) != MOE_OK) return st;
+    char* base = static_cast<char*>(ws);
+    const void* plan = plan_ws ? plan_ws : static_cast<const void*>(base + F.plan_base);
+    if (!plan_ws) {
+        const hipError_t e = launch_route(*shape, topk_idx, plan_ptrs(F.plan, base + F.plan_base),
+                                          static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    if ((st = moe_linear1(shape, x, x_sf, topk_w, w1, w1_sf, plan, ws, ws_bytes, stream)) != MOE_OK) return st;
+    if ((st = moe_linear2(shape, w2, w2_sf, plan, ws, ws_bytes, stream)) != MOE_OK) return st;
+    return moe_combine(shape, plan, ws, ws_bytes, y, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Internal declarations shared by the library's translation units: workspace
+// layout, kernel launchers and small device helpers for gfx950.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopk = 64;
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Offsets (bytes) of each table inside a plan workspace.
+struct PlanLayout {
+    int64_t cap = 0, max_blocks = 0;
+    size_t scalars = 0, counts = 0, offsets = 0, slot = 0, row_token = 0, row_topk = 0,
+           block_expert = 0, slack = 0, pull_order = 0, total = 0;
+};
+
+inline int64_t capacity_rows(const moe_shape& s) {
+    const int64_t raw = (int64_t)s.num_tokens * s.topk + (int64_t)s.num_experts * (s.block_m - 1);
+    return (raw + s.block_m - 1) / s.block_m * s.block_m;
+}
+
+inline PlanLayout plan_layout(const moe_shape& s) {
+    PlanLayout L;
+    L.cap = capacity_rows(s);
+    L.max_blocks = L.cap / s.block_m;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, kAlign); return at; };
+    L.scalars = take(16 * sizeof(int32_t));
+    L.counts = take((size_t)s.num_experts * 4);
+    L.offsets = take((size_t)(s.num_experts + 1) * 4);
+    L.slot = take((size_t)s.num_tokens * s.topk * 4);
+    L.row_token = take((size_t)L.cap * 4);
+    L.row_topk = take((size_t)L.cap * 4);
+    L.block_expert = take((size_t)L.max_blocks * 4);
+    L.slack = take((size_t)L.max_blocks * 4);
+    L.pull_order = take((size_t)s.num_tokens * 4);
+    L.total = o;
+    return L;
+}
+
+// Offsets (bytes) inside a forward workspace: the plan region first.
+struct ForwardLayout {
+    PlanLayout plan;
+    size_t plan_base = 0, h_q = 0, h_sf = 0, yslot = 0, total = 0;
+};
+
+inline ForwardLayout forward_layout(const moe_shape& s) {
+    ForwardLayout F;
+    F.plan = plan_layout(s);
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, kAlign); return at; };
+    F.plan_base = take(F.plan.total);
+    F.h_q = take((size_t)F.plan.cap * s.intermediate);
+    F.h_sf = take((size_t)F.plan.cap * (s.intermediate / 32));
+    F.yslot = take((size_t)F.plan.cap * s.hidden * 2);
+    F.total = o;
+    return F;
+}
+
+struct PlanPtrs {
+    int32_t *scalars, *counts, *offsets, *slot, *row_token, *row_topk, *block_expert, *slack, *pull_order;
+};
+
+inline PlanPtrs plan_ptrs(const PlanLayout& L, void* base) {
+    char* b = static_cast<char*>(base);
+    return PlanPtrs{reinterpret_cast<int32_t*>(b + L.scalars),      reinterpret_cast<int32_t*>(b + L.counts),
+                    reinterpret_cast<int32_t*>(b + L.offsets),      reinterpret_cast<int32_t*>(b + L.slot),
+                    reinterpret_cast<int32_t*>(b + L.row_token),    reinterpret_cast<int32_t*>(b + L.row_topk),
+                    reinterpret_cast<int32_t*>(b + L.block_expert), reinterpret_cast<int32_t*>(b + L.slack),
+                    reinterpret_cast<int32_t*>(b + L.pull_order)};
+}
+
+// ---- launchers (each enqueues on `stream` and returns the launch status) ----
+hipError_t launch_route(const moe_shape& s, const int64_t* topk_idx, const PlanPtrs& p, hipStream_t stream);
+
+struct GemmProblem {
+    const moe_shape* shape;
+    const PlanPtrs* plan;
+    int64_t cap;
+};
+hipError_t launch_linear1(const GemmProblem& g, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
+                          const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf,
+                          hipStream_t stream);
+hipError_t launch_linear2(const GemmProblem& g, const uint8_t* h_q, const uint8_t* h_sf, const uint8_t* w2,
+                          const uint8_t* w2_sf, uint16_t* yslot, hipStream_t stream);
+hipError_t launch_combine(const moe_shape& s, const uint16_t* yslot, const int32_t* slot, uint16_t* y,
+                          hipStream_t stream);
+
+}  // namespace moe

@@ -150,7 +150,8 @@ def make_inputs(w: Workload | str, device="cpu", num_tokens: int | None = None, 
         x[perm[: int(T * w.outlier_frac)]] *= w.outlier_scale
     xq, xsf = quantize_e4m3_blocks(x) if T > 0 else (torch.zeros(0, H, dtype=torch.uint8, device=device),
                                                    torch.zeros(0, H // 32, dtype=torch.uint8, device=device))
-    out = {"x": xq, "x_sf": xsf, "topk_idx": ids, "topk_w": tw}
+    out = {"x": xq.contiguous(), "x_sf": xsf.contiguous(), "topk_idx": ids.contiguous(),
+           "topk_w": tw.contiguous()}
     if with_weights:
         out.update(make_weights(w, device, weight_seed))
     return out

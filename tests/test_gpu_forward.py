@@ -1,0 +1,136 @@
+"""GPU parity of the whole forward (moe_forward) against the CPU oracle.
+
+Small shapes are compared in full (FP8 intermediates of every valid row, y
+of every token); the full-size workloads compare sampled tokens, whose rows
+the oracle computes one by one, plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+from moe_expert_ffn_plan_amd import binding as B
+from moe_expert_ffn_plan_amd import inputs
+from oracle.forward import dequant_fp4_rows, dequant_fp8_rows, forward_ref, forward_tokens
+from oracle.routing import plan_ref
+from parity import (assert_fp8_gate, assert_plan_equal, assert_y_gate, bf16_to_f32, gpu_plan_to_numpy,
+                    linear1_cancellation)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(w, d, dev, expert_begin=0, separate_plan=True):
+    T = d["x"].shape[0]
+    s = B.shape_of(w, num_tokens=T, expert_begin=expert_begin)
+    g = {k: v.to(dev) for k, v in d.items()}
+    y = torch.full((T, w.hidden), -1, dtype=torch.int16, device=dev)
+    ws = torch.full((B.forward_workspace_bytes(s),), 0x5A, dtype=torch.uint8, device=dev)
+    plan_ws = None
+    if separate_plan:
+        plan_ws = torch.full((B.plan_workspace_bytes(s),), 0x5A, dtype=torch.uint8, device=dev)
+        B.plan(s, g["topk_idx"], plan_ws)
+    B.forward(s, g["x"], g["x_sf"], g["topk_idx"], g["topk_w"], g["w1"], g["w1_sf"], g["w2"], g["w2_sf"], y, ws,
+              plan_ws=plan_ws)
+    torch.cuda.synchronize()
+    fv = B.forward_view(s, ws)
+    pv = B.plan_view(s, plan_ws if plan_ws is not None else fv["plan_ws"])
+    return {"y": bf16_to_f32(y.cpu().numpy()), "h_q": fv["h_q"].cpu().numpy(), "h_sf": fv["h_sf"].cpu().numpy(),
+            "plan": gpu_plan_to_numpy(pv, T, w.topk)}
+
+
+def check_full(w, d_cpu, out, expert_begin=0):
+    d = inputs.to_numpy(d_cpu)
+    ref = forward_ref(d["x"], d["x_sf"], d["topk_idx"] - expert_begin, d["topk_w"], d["w1"], d["w1_sf"], d["w2"],
+                      d["w2_sf"], num_experts=w.num_experts, expert_begin=0, block_m=w.block_m)
+    p = ref["plan"]
+    assert_plan_equal(out["plan"], plan_ref(d["topk_idx"], w.num_experts, expert_begin, w.block_m))
+    valid = p.row_token >= 0
+    cancel = np.zeros((p.r_pad, w.intermediate), bool)
+    for e in range(w.num_experts):
+        rows = np.arange(p.offsets[e], p.offsets[e] + p.counts[e])
+        if rows.size:
+            tok = p.row_token[rows]
+            cancel[rows] = linear1_cancellation(dequant_fp8_rows(d["x"][tok], d["x_sf"][tok]),
+                                                dequant_fp4_rows(d["w1"][e], d["w1_sf"][e]))
+    assert_fp8_gate(out["h_q"][:p.r_pad][valid], out["h_sf"][:p.r_pad][valid], ref["h_q"][valid],
+                    ref["h_sf"][valid], cancel[valid], w.name)
+    assert_y_gate(out["y"], ref["y"], w.name)
+    return ref
+
+
+SMALL = {
+    # several M-tiles per expert, ragged last blocks, all block_m values, non-local ids
+    "small_bm16": inputs.Workload("small_bm16", 200, 512, 256, 6, 10, 4, 16, "uniform", seed=11, weight_seed=21),
+    "small_bm32": inputs.Workload("small_bm32", 384, 1024, 512, 8, 12, 4, 32, "uniform", seed=12, weight_seed=22),
+    "small_bm64": inputs.Workload("small_bm64", 700, 768, 384, 5, 5, 3, 64, "uniform", seed=13, weight_seed=23),
+    "small_bm128": inputs.Workload("small_bm128", 900, 512, 640, 7, 9, 5, 128, "uniform", seed=14,
+                                   weight_seed=24),
+    "small_skewed": inputs.Workload("small_skewed", 1500, 1024, 256, 8, 64, 8, 128, "zipf", 0.1, 50.0, seed=15,
+                                    weight_seed=25),
+}
+
+
+@pytest.mark.parametrize("name", ["tiny", *SMALL])
+def test_forward_small_full(gpu, name):
+    w = inputs.WORKLOADS.get(name) or SMALL[name]
+    print(f"forward parity: {name} T={w.num_tokens} H={w.hidden} I={w.intermediate} E={w.num_experts} "
+          f"k={w.topk} bm={w.block_m}", flush=True)
+    d = inputs.make_inputs(w, device="cpu")
+    out = run_gpu(w, d, gpu)
+    check_full(w, d, out)
+
+
+def test_forward_internal_plan_and_expert_begin(gpu):
+    w = SMALL["small_bm32"]
+    d = inputs.make_inputs(w, device="cpu")
+    d["topk_idx"] = d["topk_idx"] + 40          # local experts are ids [40, 48)
+    print("forward parity: expert_begin=40, plan built inside moe_forward", flush=True)
+    out = run_gpu(w, d, gpu, expert_begin=40, separate_plan=False)
+    check_full(w, d, out, expert_begin=40)
+
+
+def test_forward_tp_slice_full(gpu):
+    w = inputs.WORKLOADS["tp_slice"]
+    print("forward parity: tp_slice full size, whole output", flush=True)
+    d = inputs.make_inputs(w, device=gpu)
+    out = run_gpu(w, d, gpu)
+    check_full(w, {k: v.cpu() for k, v in d.items()}, out)
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill", "skewed"])
+def test_forward_large_sampled(gpu, name):
+    w = inputs.WORKLOADS[name]
+    print(f"forward parity: {name} full size, sampled tokens", flush=True)
+    d = inputs.make_inputs(w, device=gpu)
+    out = run_gpu(w, d, gpu)
+    dn = inputs.to_numpy(d)
+    ids = dn["topk_idx"]
+    local = (ids >= 0) & (ids < w.num_experts)
+    # routing tables in full
+    p = plan_ref(ids, w.num_experts, 0, w.block_m)
+    assert_plan_equal(out["plan"], p)
+    # tokens without a local hit give exactly +0
+    none = ~local.any(axis=1)
+    assert np.all(out["y"][none] == 0) and not np.any(np.signbit(out["y"][none]))
+    # sampled tokens: a few with hits on a small set of experts (bounds the oracle's work)
+    rng = np.random.default_rng(7)
+    cand = np.nonzero(local.any(axis=1))[0]
+    chosen, experts = [], set()
+    for t in rng.permutation(cand):
+        es = set(ids[t][local[t]].tolist())
+        if len(experts | es) <= 6:
+            chosen.append(int(t))
+            experts |= es
+        if len(chosen) >= 12:
+            break
+    chosen = np.array(sorted(chosen))
+    yref, hits = forward_tokens(chosen, dn["x"], dn["x_sf"], ids, dn["topk_w"], dn["w1"], dn["w1_sf"], dn["w2"],
+                                dn["w2_sf"], num_experts=w.num_experts, expert_begin=0)
+    q_g = np.stack([out["h_q"][p.slot[t, j]] for (t, j) in hits])
+    s_g = np.stack([out["h_sf"][p.slot[t, j]] for (t, j) in hits])
+    q_r = np.stack([v[0] for v in hits.values()])
+    s_r = np.stack([v[1] for v in hits.values()])
+    w1_deq = {e: dequant_fp4_rows(dn["w1"][e], dn["w1_sf"][e]) for e in experts}
+    cancel = np.concatenate([linear1_cancellation(dequant_fp8_rows(dn["x"][[t]], dn["x_sf"][[t]]),
+                                                  w1_deq[int(ids[t, j])]) for (t, j) in hits])
+    assert_fp8_gate(q_g, s_g, q_r, s_r, cancel, name)
+    assert_y_gate(out["y"][chosen], yref, name)
