@@ -63,6 +63,8 @@ def main() -> int:
     ap.add_argument("--weight-copies", type=int, default=3)
     ap.add_argument("--cpu-sample-tokens", type=int, default=384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--host-inputs", action="store_true",
+                    help="draw the synthetic inputs on the CPU and copy them (fewer torch GPU kernels, for profilers)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs one GPU's share of the MoE layer; --gpus {args.gpus} is not supported "
@@ -79,10 +81,15 @@ def main() -> int:
     dev = torch.device("cuda:0")
     w = inputs.WORKLOADS[args.workload]
     s = B.shape_of(w)
-    d = inputs.make_inputs(w, device=dev)
-    weights = [{k: d[k] for k in ("w1", "w1_sf", "w2", "w2_sf")}]
+    gen_dev = "cpu" if args.host_inputs else dev
+    d = {k: v.to(dev) for k, v in inputs.make_inputs(w, device=gen_dev).items()}
+    # one-time weight re-layout (untimed, like the pages' weight transform)
+    weights = [B.prepare_all(s, d)]
     for c in range(1, args.weight_copies):
-        weights.append(inputs.make_weights(w, device=dev, weight_seed=w.weight_seed + 1000 * c))
+        wc = inputs.make_weights(w, device=gen_dev, weight_seed=w.weight_seed + 1000 * c)
+        weights.append(B.prepare_all(s, {k: v.to(dev) for k, v in wc.items()}))
+        del wc
+    torch.cuda.synchronize()
     plan_ws = torch.empty(B.plan_workspace_bytes(s), dtype=torch.uint8, device=dev)
     ws = torch.empty(B.forward_workspace_bytes(s), dtype=torch.uint8, device=dev)
     y = torch.empty(w.num_tokens, w.hidden, dtype=torch.bfloat16, device=dev)
@@ -137,7 +144,7 @@ def main() -> int:
            "kernel_ms": {k: round(v, 4) for k, v in kern_ms.items()},
            "roofline": roofline}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, {k: v for k, v in d.items()}, args.cpu_sample_tokens)
+        out["cpu_baseline"] = cpu_baseline(w, d, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)
     return 0
 

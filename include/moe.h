@@ -132,13 +132,16 @@ MOE_API int moe_plan_view_get(const moe_shape* shape, void* plan_ws, moe_plan_vi
  *   topk_idx int64 [T, k]        global expert ids
  *   topk_w   float [T, k]        routing weights (applied in the Linear1
  *                                epilogue, walk-through section 4.6)
- *   w1       uint8 [E, 2I, H/2]  FP4 E2M1 pairs, even K in the low nibble;
- *                                rows interleave gate/up by 8:
- *                                [g0..7, u0..7, g8..15, u8..15, ...]
- *                                (walk-through section 7.3)
- *   w1_sf    uint8 [E, 2I, H/32] UE8M0, one per row per 32 K
- *   w2       uint8 [E, H, I/2]   FP4 E2M1 pairs
- *   w2_sf    uint8 [E, H, I/32]  UE8M0
+ *   w1, w1_sf, w2, w2_sf         the expert weights in the TILED layout made
+ *                                once by moe_prepare_weights (below) from the
+ *                                plain layout:
+ *     plain w1    uint8 [E, 2I, H/2]  FP4 E2M1 pairs, even K in the low
+ *                                     nibble; rows interleave gate/up by 8:
+ *                                     [g0..7, u0..7, g8..15, u8..15, ...]
+ *                                     (walk-through section 7.3)
+ *     plain w1_sf uint8 [E, 2I, H/32] UE8M0, one per row per 32 K
+ *     plain w2    uint8 [E, H, I/2]   FP4 E2M1 pairs
+ *     plain w2_sf uint8 [E, H, I/32]  UE8M0
  * Output:
  *   y        uint16 [T, H]       BF16; y[t] = sum over t's local top-k
  *                                entries (j ascending, FP32) of the BF16
@@ -149,6 +152,23 @@ MOE_API int moe_plan_view_get(const moe_shape* shape, void* plan_ws, moe_plan_vi
  *   the FP8 Linear2 input (and its scales) and the BF16 per-slot Linear2
  *   rows between kernels. */
 MOE_API int moe_forward_workspace_bytes(const moe_shape* shape, size_t* bytes);
+
+/* One-time weight re-layout (the analog of the pages' weight transform,
+ * SymmBuffer page section 7: their forward also consumes weights prepared
+ * once for the kernel).  which = 1: W1 (N = 2I rows, K = H); which = 2: W2
+ * (N = H, K = I).  Reads the plain layout (w [E, N, K/2], w_sf [E, N, K/32])
+ * and writes the tiled layout, a permutation of the same bytes (w_tiled has
+ * E*N*K/2 bytes, w_sf_tiled E*N*K/32):
+ *   w_tiled    [E][N/256][K/128][1024 slots of 16 B]: slot p holds bytes
+ *              [kt*64 + q*16, +16) of tile column c = p >> 2, with
+ *              q = (p & 3) ^ ((c >> 2) & 3);
+ *   w_sf_tiled [E][N/256][K/128][256 columns][4 B]: the column's four
+ *              scale bytes for that K-step.
+ * Enqueued on `stream`; buffers owned by the caller; in and out must not
+ * overlap. */
+MOE_API int moe_prepare_weights(const moe_shape* shape, int which,
+                const uint8_t* w, const uint8_t* w_sf,
+                uint8_t* w_tiled, uint8_t* w_sf_tiled, void* stream);
 MOE_API int moe_forward(const moe_shape* shape,
                 const uint8_t* x, const uint8_t* x_sf,
                 const int64_t* topk_idx, const float* topk_w,
@@ -184,7 +204,9 @@ MOE_API int moe_combine(const moe_shape* shape, const void* plan_ws,
 /* Device pointers to the intermediates inside a forward workspace, for
  * tests (no GPU work):
  *   h_q   uint8  [cap, I]     FP8 E4M3 Linear2 input (SwiGLU x w, requantised)
- *   h_sf  uint8  [cap, I/32]  its UE8M0 scales
+ *   h_sf  uint8  [cap/block_m][I/128][block_m][4]  its UE8M0 scales: the
+ *         scale of row r, 32-channel group g is at
+ *         [r / block_m][g / 4][r % block_m][g % 4]
  *   yslot uint16 [cap, H]     BF16 Linear2 output per slot row
  *   plan  the plan region used when moe_forward got plan_ws == NULL
  * Rows of padding (and rows >= R_pad) hold unspecified values. */

@@ -45,6 +45,7 @@ _lib = None
 
 EXPORTS = ["moe_capacity_rows", "moe_plan_workspace_bytes", "moe_plan", "moe_plan_view_get",
            "moe_forward_workspace_bytes", "moe_forward", "moe_linear1", "moe_linear2", "moe_combine",
+           "moe_prepare_weights",
            "moe_forward_view_get", "moe_device_supported", "moe_status_str"]
 
 
@@ -63,6 +64,7 @@ def lib() -> ctypes.CDLL:
         L.moe_plan.argtypes = [S, VP, VP, SZ, VP]
         L.moe_plan_view_get.argtypes = [S, VP, P(PlanView)]
         L.moe_forward.argtypes = [S, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_prepare_weights.argtypes = [S, ctypes.c_int, VP, VP, VP, VP, VP]
         L.moe_linear1.argtypes = [S, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_linear2.argtypes = [S, VP, VP, VP, VP, SZ, VP]
         L.moe_combine.argtypes = [S, VP, VP, SZ, VP, VP]
@@ -170,6 +172,33 @@ def forward(shape: MoeShape, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y,
     _check("moe_forward", st)
 
 
+def prepare_weights(shape: MoeShape, which: int, w, w_sf, stream=None):
+    """Tiled copies (new tensors) of one plain weight tensor and its scales (which = 1: W1, 2: W2)."""
+    H, I, E = shape.hidden, shape.intermediate, shape.num_experts
+    N, K = (2 * I, H) if which == 1 else (H, I)
+    dev = w.device
+    _ptr(w, torch.uint8, "w", dev, E * N * K // 2)
+    _ptr(w_sf, torch.uint8, "w_sf", dev, E * N * K // 32)
+    wt = torch.empty(E * N * K // 2, dtype=torch.uint8, device=dev)
+    st_ = torch.empty(E * N * K // 32, dtype=torch.uint8, device=dev)
+    st = lib().moe_prepare_weights(ctypes.byref(shape), which, _ptr(w, torch.uint8, "w"), _ptr(w_sf, torch.uint8, "w_sf"),
+                                   _ptr(wt, torch.uint8, "w_tiled"), _ptr(st_, torch.uint8, "w_sf_tiled"), _stream(stream))
+    _check("moe_prepare_weights", st)
+    return wt, st_
+
+
+def prepare_all(shape: MoeShape, d: dict, stream=None) -> dict:
+    """Tiled W1/W2 (keys w1, w1_sf, w2, w2_sf) from a dict holding the plain ones."""
+    w1, w1_sf = prepare_weights(shape, 1, d["w1"], d["w1_sf"], stream)
+    w2, w2_sf = prepare_weights(shape, 2, d["w2"], d["w2_sf"], stream)
+    return {"w1": w1, "w1_sf": w1_sf, "w2": w2, "w2_sf": w2_sf}
+
+
+def untile_row_scales(tiled: torch.Tensor, cap: int, k: int, block_m: int) -> torch.Tensor:
+    """[cap/bm][k/128][bm][4] per-row-block scales -> plain [cap, k/32] (for tests and inspection)."""
+    return tiled.view(cap // block_m, k // 128, block_m, 4).permute(0, 2, 1, 3).reshape(cap, k // 32)
+
+
 def linear1(shape: MoeShape, x, x_sf, topk_w, w1, w1_sf, plan_ws, ws, stream=None) -> None:
     T, H, I, E, k = shape.num_tokens, shape.hidden, shape.intermediate, shape.num_experts, shape.topk
     dev, u8 = ws.device, torch.uint8
@@ -225,6 +254,6 @@ def forward_view(shape: MoeShape, ws: torch.Tensor) -> dict:
     cap, H, I = v.capacity_rows, shape.hidden, shape.intermediate
     plan_off = v.plan - ws.data_ptr()
     return {"h_q": _slice(ws, v.h_q, torch.uint8, cap * I).view(cap, I),
-            "h_sf": _slice(ws, v.h_sf, torch.uint8, cap * I // 32).view(cap, I // 32),
+            "h_sf": untile_row_scales(_slice(ws, v.h_sf, torch.uint8, cap * I // 32), cap, I, shape.block_m),
             "yslot": _slice(ws, v.yslot, torch.int16, cap * H).view(cap, H),
             "plan_ws": ws[plan_off:], "capacity_rows": cap}

@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
-SOURCES = ["moe_route.hip", "moe_gemm.hip", "moe_combine.hip", "moe_api.hip"]
+SOURCES = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def hipcc() -> str:

@@ -138,6 +138,22 @@ int moe_plan(const moe_shape* shape, const int64_t* topk_idx, void* plan_ws, siz
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+int moe_prepare_weights(const moe_shape* shape, int which, const uint8_t* w, const uint8_t* w_sf, uint8_t* w_tiled,
+                        uint8_t* w_sf_tiled, void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (which != 1 && which != 2) return MOE_ERR_SHAPE;
+    if (!w || !w_sf || !w_tiled || !w_sf_tiled) return MOE_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(w_tiled, 16) || !aligned(w_sf, 4) || !aligned(w_sf_tiled, 4))
+        return MOE_ERR_ALIGN;
+    if ((st = check_arch_current()) != MOE_OK) return st;
+    const int N = which == 1 ? 2 * shape->intermediate : shape->hidden;
+    const int K = which == 1 ? shape->hidden : shape->intermediate;
+    const hipError_t e = launch_tile_weights(N, K, shape->num_experts, w, w_sf, w_tiled, w_sf_tiled,
+                                             static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 int moe_linear1(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
                 const uint8_t* w1, const uint8_t* w1_sf, const void* plan_ws, void* ws, size_t ws_bytes,
                 void* stream) {
@@ -153,9 +169,19 @@ int moe_linear1(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, c
     if ((st = check_arch_current()) != MOE_OK) return st;
     const PlanPtrs p = plan_ptrs(F.plan, const_cast<void*>(plan_ws));
     char* base = static_cast<char*>(ws);
-    const GemmProblem g{shape, &p, F.plan.cap};
-    const hipError_t e = launch_linear1(g, x, x_sf, topk_w, w1, w1_sf, reinterpret_cast<uint8_t*>(base + F.h_q),
-                                        reinterpret_cast<uint8_t*>(base + F.h_sf), static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int nt1 = 2 * shape->intermediate / gemm_bn(2 * shape->intermediate);
+    const int nt2 = shape->hidden / gemm_bn(shape->hidden);
+    uint32_t* x_sf_tiled = reinterpret_cast<uint32_t*>(base + F.x_sf);
+    float* row_w = reinterpret_cast<float*>(base + F.row_w);
+    int32_t* tiles1 = reinterpret_cast<int32_t*>(base + F.tiles1);
+    int32_t* tiles2 = reinterpret_cast<int32_t*>(base + F.tiles2);
+    hipError_t e = launch_prep_linear1(*shape, x_sf, topk_w, p, F.plan.cap, nt1, nt2, x_sf_tiled, row_w, tiles1,
+                                       tiles2, s);
+    const GemmProblem g{shape, &p, F.plan.cap, tiles1, row_w};
+    if (e == hipSuccess)
+        e = launch_linear1(g, x, reinterpret_cast<const uint8_t*>(x_sf_tiled), w1, w1_sf,
+                           reinterpret_cast<uint8_t*>(base + F.h_q), reinterpret_cast<uint8_t*>(base + F.h_sf), s);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -172,7 +198,7 @@ int moe_linear2(const moe_shape* shape, const uint8_t* w2, const uint8_t* w2_sf,
     if ((st = check_arch_current()) != MOE_OK) return st;
     const PlanPtrs p = plan_ptrs(F.plan, const_cast<void*>(plan_ws));
     char* base = static_cast<char*>(ws);
-    const GemmProblem g{shape, &p, F.plan.cap};
+    const GemmProblem g{shape, &p, F.plan.cap, reinterpret_cast<const int32_t*>(base + F.tiles2), nullptr};
     const hipError_t e = launch_linear2(g, reinterpret_cast<uint8_t*>(base + F.h_q),
                                         reinterpret_cast<uint8_t*>(base + F.h_sf), w2, w2_sf,
                                         reinterpret_cast<uint16_t*>(base + F.yslot), static_cast<hipStream_t>(stream));

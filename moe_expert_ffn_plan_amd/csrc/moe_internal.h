@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/moe.h"
 
 namespace moe {
@@ -50,8 +52,12 @@ inline PlanLayout plan_layout(const moe_shape& s) {
 // Offsets (bytes) inside a forward workspace: the plan region first.
 struct ForwardLayout {
     PlanLayout plan;
-    size_t plan_base = 0, h_q = 0, h_sf = 0, yslot = 0, total = 0;
+    size_t plan_base = 0, x_sf = 0, row_w = 0, tiles1 = 0, tiles2 = 0, h_q = 0, h_sf = 0, yslot = 0, total = 0;
+    int64_t max_tiles1 = 0, max_tiles2 = 0;
 };
+
+// Tile widths of the two GEMMs: 512 columns when N allows it, else 256.
+inline int gemm_bn(int n) { return n % 512 == 0 ? 512 : 256; }
 
 inline ForwardLayout forward_layout(const moe_shape& s) {
     ForwardLayout F;
@@ -59,6 +65,12 @@ inline ForwardLayout forward_layout(const moe_shape& s) {
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, kAlign); return at; };
     F.plan_base = take(F.plan.total);
+    F.x_sf = take((size_t)F.plan.cap * (s.hidden / 32));
+    F.row_w = take((size_t)F.plan.cap * 4);
+    F.max_tiles1 = F.plan.max_blocks * (2 * s.intermediate / gemm_bn(2 * s.intermediate));
+    F.max_tiles2 = F.plan.max_blocks * (s.hidden / gemm_bn(s.hidden));
+    F.tiles1 = take((size_t)F.max_tiles1 * 8);
+    F.tiles2 = take((size_t)F.max_tiles2 * 8);
     F.h_q = take((size_t)F.plan.cap * s.intermediate);
     F.h_sf = take((size_t)F.plan.cap * (s.intermediate / 32));
     F.yslot = take((size_t)F.plan.cap * s.hidden * 2);
@@ -86,12 +98,21 @@ struct GemmProblem {
     const moe_shape* shape;
     const PlanPtrs* plan;
     int64_t cap;
+    const int32_t* tiles;  // tile list of this GEMM (written by the Linear1 prep kernel)
+    const float* row_w;    // per-row top-k weights (Linear1 only)
 };
-hipError_t launch_linear1(const GemmProblem& g, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
+// x_sf_tiled / h_sf: activation scales in the per-row-block layout [cap/BM][K/128][BM][4];
+// w*, w*_sf: weights in the tiled layout of moe_prepare.hip.
+hipError_t launch_linear1(const GemmProblem& g, const uint8_t* x, const uint8_t* x_sf_tiled,
                           const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf,
                           hipStream_t stream);
 hipError_t launch_linear2(const GemmProblem& g, const uint8_t* h_q, const uint8_t* h_sf, const uint8_t* w2,
                           const uint8_t* w2_sf, uint16_t* yslot, hipStream_t stream);
+hipError_t launch_tile_weights(int N, int K, int E, const uint8_t* w, const uint8_t* w_sf, uint8_t* w_out,
+                               uint8_t* sf_out, hipStream_t stream);
+hipError_t launch_prep_linear1(const moe_shape& s, const uint8_t* x_sf, const float* topk_w, const PlanPtrs& p,
+                               int64_t cap, int nt1, int nt2, uint32_t* xsf_out, float* row_w, int32_t* tiles1,
+                               int32_t* tiles2, hipStream_t stream);
 hipError_t launch_combine(const moe_shape& s, const uint16_t* yslot, const int32_t* slot, uint16_t* y,
                           hipStream_t stream);
 

@@ -22,6 +22,7 @@ def run_gpu(w, d, dev, expert_begin=0, separate_plan=True):
     T = d["x"].shape[0]
     s = B.shape_of(w, num_tokens=T, expert_begin=expert_begin)
     g = {k: v.to(dev) for k, v in d.items()}
+    g.update(B.prepare_all(s, g))
     y = torch.full((T, w.hidden), -1, dtype=torch.int16, device=dev)
     ws = torch.full((B.forward_workspace_bytes(s),), 0x5A, dtype=torch.uint8, device=dev)
     plan_ws = None
@@ -94,6 +95,34 @@ def test_forward_tp_slice_full(gpu):
     d = inputs.make_inputs(w, device=gpu)
     out = run_gpu(w, d, gpu)
     check_full(w, {k: v.cpu() for k, v in d.items()}, out)
+
+
+def _tile_reference(w, w_sf, N, K):
+    """The documented tiled layout, built with NumPy index arithmetic."""
+    E = w.shape[0]
+    NT, KT = N // 256, K // 128
+    p = np.arange(1024)
+    c = p >> 2
+    q = (p & 3) ^ ((c >> 2) & 3)
+    chunks = w.reshape(E, NT, 256, KT, 4, 16)                       # [e, nt, col, kt, chunk, 16]
+    data = chunks[:, :, c, :, q, :]                                  # [1024, e, nt, kt, 16] (advanced dims first)
+    data = np.moveaxis(data, 0, 3).reshape(-1)                       # [e, nt, kt, 1024, 16]
+    sf = w_sf.reshape(E, NT, 256, KT, 4).transpose(0, 1, 3, 2, 4).reshape(-1)
+    return data, sf
+
+
+@pytest.mark.parametrize("which", [1, 2])
+def test_prepare_weights_layout(gpu, which):
+    w = SMALL["small_bm128"]
+    d = inputs.make_inputs(w, device="cpu")
+    s = B.shape_of(w)
+    key = "w1" if which == 1 else "w2"
+    N, K = (2 * w.intermediate, w.hidden) if which == 1 else (w.hidden, w.intermediate)
+    wt, sft = B.prepare_weights(s, which, d[key].to(gpu), d[key + "_sf"].to(gpu))
+    torch.cuda.synchronize()
+    want_w, want_sf = _tile_reference(d[key].numpy(), d[key + "_sf"].numpy(), N, K)
+    assert np.array_equal(wt.cpu().numpy(), want_w)
+    assert np.array_equal(sft.cpu().numpy(), want_sf)
 
 
 @pytest.mark.parametrize("name", ["decode", "prefill", "skewed"])
