@@ -19,10 +19,13 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Offsets (bytes) of each table inside a plan workspace.
+// Routing of large inputs runs as three kernels over groups of kRouteTokensPerGroup tokens.
+constexpr int kRouteTokensPerGroup = 256;
+
 struct PlanLayout {
-    int64_t cap = 0, max_blocks = 0;
+    int64_t cap = 0, max_blocks = 0, groups = 0;
     size_t scalars = 0, counts = 0, offsets = 0, slot = 0, row_token = 0, row_topk = 0,
-           block_expert = 0, slack = 0, pull_order = 0, total = 0;
+           block_expert = 0, slack = 0, pull_order = 0, group_counts = 0, total = 0;
 };
 
 inline int64_t capacity_rows(const moe_shape& s) {
@@ -45,6 +48,8 @@ inline PlanLayout plan_layout(const moe_shape& s) {
     L.block_expert = take((size_t)L.max_blocks * 4);
     L.slack = take((size_t)L.max_blocks * 4);
     L.pull_order = take((size_t)s.num_tokens * 4);
+    L.groups = (s.num_tokens + kRouteTokensPerGroup - 1) / kRouteTokensPerGroup;
+    L.group_counts = take((size_t)L.groups * s.num_experts * 2 * 4);  // hit and pull counts per group
     L.total = o;
     return L;
 }
@@ -79,7 +84,8 @@ inline ForwardLayout forward_layout(const moe_shape& s) {
 }
 
 struct PlanPtrs {
-    int32_t *scalars, *counts, *offsets, *slot, *row_token, *row_topk, *block_expert, *slack, *pull_order;
+    int32_t *scalars, *counts, *offsets, *slot, *row_token, *row_topk, *block_expert, *slack, *pull_order,
+        *group_counts;
 };
 
 inline PlanPtrs plan_ptrs(const PlanLayout& L, void* base) {
@@ -88,7 +94,7 @@ inline PlanPtrs plan_ptrs(const PlanLayout& L, void* base) {
                     reinterpret_cast<int32_t*>(b + L.offsets),      reinterpret_cast<int32_t*>(b + L.slot),
                     reinterpret_cast<int32_t*>(b + L.row_token),    reinterpret_cast<int32_t*>(b + L.row_topk),
                     reinterpret_cast<int32_t*>(b + L.block_expert), reinterpret_cast<int32_t*>(b + L.slack),
-                    reinterpret_cast<int32_t*>(b + L.pull_order)};
+                    reinterpret_cast<int32_t*>(b + L.pull_order), reinterpret_cast<int32_t*>(b + L.group_counts)};
 }
 
 // ---- launchers (each enqueues on `stream` and returns the launch status) ----

@@ -18,6 +18,14 @@
 // second counting sort of tokens keyed by their smallest local expert (a
 // token's smallest slot lies in the range of its smallest expert, and tokens
 // of one expert are in ascending t there).
+//
+// Large inputs use three kernels instead, so the work spreads over many CUs:
+// route_count_kernel (per group of 256 tokens: hit counts per expert and
+// pull counts per smallest expert), route_scan_kernel (one workgroup: bases
+// of every group, counts, padded offsets, block tables, padding rows) and
+// route_scatter_kernel (per group: the same stable ballot-match scatter,
+// with each wave owning a contiguous 64-token slice).  Both paths produce
+// identical tables.
 #include "moe_internal.h"
 
 namespace moe {
@@ -232,13 +240,238 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
     }
 }
 
+// ---------------------------------------------------------------- multi-group path
+constexpr int kGThreads = 256;
+constexpr int kGWaves = kGThreads / 64;
+constexpr int kWaveTokens = kRouteTokensPerGroup / kGWaves;  // contiguous tokens per wave
+
+// Loads the group's top-k ids once (coalesced, 8 loads in flight per thread) as local expert
+// ids, -1 when not local, into LDS `le` [tokens * k].
+__device__ __forceinline__ void load_group_experts(const int64_t* __restrict__ ids, int64_t h0, int64_t h1, int k,
+                                                   int64_t begin, int E, int16_t* le) {
+    const int n = (int)(h1 - h0);
+    for (int base = 0; base < n; base += 8 * kGThreads) {
+        int64_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = base + u * kGThreads + threadIdx.x;
+            v[u] = i < n ? ids[h0 + i] - begin : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = base + u * kGThreads + threadIdx.x;
+            if (i < n) le[i] = (int16_t)((v[u] >= 0 && v[u] < E) ? v[u] : -1);
+        }
+    }
+}
+
+__device__ __forceinline__ int smallest_in(const int16_t* le, int t_local, int k, int E) {
+    int emin = E;
+    for (int j = 0; j < k; ++j) {
+        const int e = le[t_local * k + j];
+        if (e >= 0 && e < emin) emin = e;
+    }
+    return emin;
+}
+
+// group_counts: [groups][E] hit counts, then [groups][E] pull counts.
+__global__ __launch_bounds__(kGThreads) void route_count_kernel(const int64_t* __restrict__ ids, int T, int k, int E,
+                                                               int expert_begin, int groups,
+                                                               int32_t* __restrict__ gcounts) {
+    extern __shared__ int32_t lds[];
+    int32_t* ch = lds;                                          // [E]
+    int32_t* cp = lds + E;                                      // [E]
+    int16_t* le = reinterpret_cast<int16_t*>(lds + 2 * E);      // [256 * k]
+    const int tid = threadIdx.x, g = blockIdx.x;
+    for (int i = tid; i < 2 * E; i += kGThreads) lds[i] = 0;
+    const int t0 = g * kRouteTokensPerGroup, t1 = min(T, t0 + kRouteTokensPerGroup);
+    load_group_experts(ids, (int64_t)t0 * k, (int64_t)t1 * k, k, expert_begin, E, le);
+    __syncthreads();
+    const int nh = (t1 - t0) * k;
+    for (int i = tid; i < nh; i += kGThreads)
+        if (le[i] >= 0) atomicAdd(&ch[le[i]], 1);
+    for (int t = tid; t < t1 - t0; t += kGThreads) {
+        const int emin = smallest_in(le, t, k, E);
+        if (emin < E) atomicAdd(&cp[emin], 1);
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kGThreads) {
+        gcounts[(size_t)g * E + e] = ch[e];
+        gcounts[((size_t)groups + g) * E + e] = cp[e];
+    }
+}
+
+// One workgroup: turns group counts into absolute group bases (slot row and pull position of the
+// group's first hit / token of each expert), and writes counts, offsets, scalars, block tables and
+// the padding rows.  Group counts go through LDS in chunks of whole groups.
+constexpr int kScanChunkWords = 8192;
+
+__global__ __launch_bounds__(kThreads) void route_scan_kernel(int E, int bm, int groups, int32_t* __restrict__ gcounts,
+                                                             PlanPtrs p) {
+    extern __shared__ int32_t lds[];
+    int32_t* soff = lds;            // [E+1] padded offsets
+    int32_t* scnt = soff + E + 1;   // [E] hit counts
+    int32_t* pbase = scnt + E;      // [E+1] pull bases
+    int32_t* ptot = pbase + E + 1;  // [E] pull counts
+    int32_t* scratch = ptot + E;    // [64]
+    int32_t* chunk = scratch + 64;  // [kScanChunkWords]
+    const int tid = threadIdx.x;
+    const int gpc = max(1, kScanChunkWords / (2 * E));  // groups per chunk
+    int run = 0, prun = 0;                              // running sums of expert `tid`
+    for (int g0 = 0; g0 < groups; g0 += gpc) {
+        const int ng = min(gpc, groups - g0);
+        for (int i = tid; i < ng * E; i += kThreads) {
+            chunk[i] = gcounts[(size_t)g0 * E + i];
+            chunk[ng * E + i] = gcounts[((size_t)groups + g0) * E + i];
+        }
+        __syncthreads();
+        if (tid < E)
+            for (int g = 0; g < ng; ++g) {
+                const int c = chunk[g * E + tid], cq = chunk[(ng + g) * E + tid];
+                chunk[g * E + tid] = run;
+                chunk[(ng + g) * E + tid] = prun;
+                run += c;
+                prun += cq;
+            }
+        __syncthreads();
+        for (int i = tid; i < ng * E; i += kThreads) {
+            gcounts[(size_t)g0 * E + i] = chunk[i];
+            gcounts[((size_t)groups + g0) * E + i] = chunk[ng * E + i];
+        }
+        __syncthreads();
+    }
+    if (tid < E) {
+        scnt[tid] = run;
+        ptot[tid] = prun;
+    }
+    const int cnt = tid < E ? run : 0;
+    const int padded = (cnt + bm - 1) / bm * bm;
+    const int incl_pad = block_inclusive_scan(padded, scratch);
+    const int incl_cnt = block_inclusive_scan(cnt, scratch);
+    const int incl_pull = block_inclusive_scan(tid < E ? prun : 0, scratch);
+    if (tid < E) {
+        soff[tid + 1] = incl_pad;
+        pbase[tid + 1] = incl_pull;
+        p.counts[tid] = cnt;
+        p.offsets[tid + 1] = incl_pad;
+    }
+    if (tid == 0) {
+        soff[0] = 0;
+        pbase[0] = 0;
+        p.offsets[0] = 0;
+    }
+    if (tid == E - 1) {
+        p.scalars[0] = incl_pad;        // R_pad
+        p.scalars[1] = incl_pull;       // n_pull
+        p.scalars[2] = incl_cnt;        // N
+        p.scalars[3] = incl_pad / bm;   // n_blocks
+    }
+    __syncthreads();
+    for (int64_t i = tid; i < (int64_t)groups * E; i += kThreads) {
+        const int e = (int)(i % E);
+        gcounts[i] += soff[e];
+        gcounts[(size_t)groups * E + i] += pbase[e];
+    }
+    const int n_blocks = soff[E] / bm;
+    for (int b = tid; b < n_blocks; b += kThreads) {
+        const int r = b * bm;
+        int lo = 0, hi = E;  // largest e with soff[e] <= r (that expert has rows)
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (soff[mid] <= r) lo = mid; else hi = mid - 1;
+        }
+        const int fill_end = soff[lo] + scnt[lo];
+        p.block_expert[b] = lo;
+        p.slack[b] = bm - max(0, min(r + bm, fill_end) - max(r, soff[lo]));
+        for (int q = max(r, fill_end); q < r + bm; ++q) {
+            p.row_token[q] = -1;
+            p.row_topk[q] = -1;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kGThreads) void route_scatter_kernel(const int64_t* __restrict__ ids, int T, int k, int E,
+                                                                 int expert_begin, int groups,
+                                                                 const int32_t* __restrict__ gcounts, PlanPtrs p) {
+    extern __shared__ int32_t lds[];
+    int32_t* wh = lds;                                           // [kGWaves][E] running hit rows
+    int32_t* wp = lds + kGWaves * E;                             // [kGWaves][E] running pull positions
+    int16_t* le = reinterpret_cast<int16_t*>(lds + 2 * kGWaves * E);  // [256 * k]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = blockIdx.x;
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    for (int i = tid; i < 2 * kGWaves * E; i += kGThreads) lds[i] = 0;
+    const int tg0 = g * kRouteTokensPerGroup, tg1 = min(T, tg0 + kRouteTokensPerGroup);
+    load_group_experts(ids, (int64_t)tg0 * k, (int64_t)tg1 * k, k, expert_begin, E, le);
+    __syncthreads();
+    const int t0 = min(tg1, tg0 + w * kWaveTokens);  // this wave's tokens [t0, t1)
+    const int t1 = min(tg1, t0 + kWaveTokens);
+    const int l0 = (t0 - tg0) * k, l1 = (t1 - tg0) * k;  // and hits (group-local)
+    for (int i = l0 + lane; i < l1; i += 64)
+        if (le[i] >= 0) atomicAdd(&wh[w * E + le[i]], 1);
+    const int tt = t0 + lane;
+    const int emin = tt < t1 ? smallest_in(le, tt - tg0, k, E) : E;
+    if (emin < E) atomicAdd(&wp[w * E + emin], 1);
+    __syncthreads();
+    for (int e = tid; e < E; e += kGThreads) {
+        int run = gcounts[(size_t)g * E + e];
+        int prun = gcounts[((size_t)groups + g) * E + e];
+        for (int ww = 0; ww < kGWaves; ++ww) {
+            const int c = wh[ww * E + e], cq = wp[ww * E + e];
+            wh[ww * E + e] = run;
+            wp[ww * E + e] = prun;
+            run += c;
+            prun += cq;
+        }
+    }
+    __syncthreads();
+    // stable scatter of this wave's hits (flat order), 64 at a time
+    const int64_t hg0 = (int64_t)tg0 * k;
+    for (int base = l0; base < l1; base += 64) {
+        const int i = base + lane;
+        const int e = i < l1 ? le[i] : -1;
+        const bool valid = e >= 0;
+        const uint64_t peers = match_peers(valid, e, nbits);
+        const int64_t h = hg0 + i;
+        if (valid) {
+            const int rank = __popcll(peers & lanes_lt());
+            const int cur = wh[w * E + e];
+            const int row = cur + rank;
+            p.slot[h] = row;
+            p.row_token[row] = (int)(h / k);
+            p.row_topk[row] = (int)(h % k);
+            if (rank == 0) wh[w * E + e] = cur + __popcll(peers);
+        } else if (i < l1) {
+            p.slot[h] = -1;
+        }
+    }
+    // pull order: this wave's tokens by smallest local expert, ascending t
+    const bool pv = emin < E;
+    const uint64_t peers = match_peers(pv, emin, nbits);
+    if (pv) {
+        const int rank = __popcll(peers & lanes_lt());
+        p.pull_order[wp[w * E + emin] + rank] = tt;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_route(const moe_shape& s, const int64_t* topk_idx, const PlanPtrs& p, hipStream_t stream) {
     const int E = s.num_experts;
-    const size_t lds = (size_t)(kWaves * E + (E + 1) + E + (E + 1) + 64) * sizeof(int32_t);
-    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kThreads), lds, stream, topk_idx, s.num_tokens, s.topk, E,
-                       s.expert_begin, s.block_m, p);
+    const int64_t hits = (int64_t)s.num_tokens * s.topk;
+    if (hits <= 4096) {
+        const size_t lds = (size_t)(kWaves * E + (E + 1) + E + (E + 1) + 64) * sizeof(int32_t);
+        hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kThreads), lds, stream, topk_idx, s.num_tokens, s.topk, E,
+                           s.expert_begin, s.block_m, p);
+        return hipGetLastError();
+    }
+    const int groups = (s.num_tokens + kRouteTokensPerGroup - 1) / kRouteTokensPerGroup;
+    const size_t le_bytes = (size_t)kRouteTokensPerGroup * s.topk * 2;
+    hipLaunchKernelGGL(route_count_kernel, dim3(groups), dim3(kGThreads), (size_t)2 * E * 4 + le_bytes, stream,
+                       topk_idx, s.num_tokens, s.topk, E, s.expert_begin, groups, p.group_counts);
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kThreads), (size_t)(4 * E + 2 + 64 + kScanChunkWords) * 4,
+                       stream, E, s.block_m, groups, p.group_counts, p);
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(groups), dim3(kGThreads), (size_t)2 * kGWaves * E * 4 + le_bytes,
+                       stream, topk_idx, s.num_tokens, s.topk, E, s.expert_begin, groups, p.group_counts, p);
     return hipGetLastError();
 }
 
