@@ -149,7 +149,7 @@ int moe_prepare_weights(const moe_shape* shape, int which, const uint8_t* w, con
     if ((st = check_arch_current()) != MOE_OK) return st;
     const int N = which == 1 ? 2 * shape->intermediate : shape->hidden;
     const int K = which == 1 ? shape->hidden : shape->intermediate;
-    const hipError_t e = launch_tile_weights(N, K, shape->num_experts, w, w_sf, w_tiled, w_sf_tiled,
+    const hipError_t e = launch_tile_weights(which, N, K, shape->num_experts, w, w_sf, w_tiled, w_sf_tiled,
                                              static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -18,24 +18,32 @@
 //    For B (FP4), lane l holds column l%16 and K [32g, 32g+32) as 16 bytes,
 //    even K in the low nibble, with its own lane's scale.  D: lane l holds
 //    column l%16, rows 4(l/16)..4(l/16)+3.
-//  * Workgroup tile BM x BN (BN = 512 with 8 waves when N allows, else 256
-//    with 4 waves), waves in a WM x WN grid.  A wave's columns are a
-//    multiple of 64 (= 32 gate/up channels = one requant scale group), so the
-//    amax reduction stays inside a wave.
 //  * Operands stream through a ring of NS LDS stages, each one 128-wide
 //    K-step of A (BM x 128 B), B (BN x 64 B) and both scale words, filled by
-//    global_load_lds DMA so in-flight tiles cost no registers.  Each wave
-//    issues exactly D_W DMA instructions per stage (every lane active, every
-//    address valid), so "stage kt has landed" is s_waitcnt vmcnt(n * D_W)
-//    with n the stages issued after it, followed by a workgroup barrier.  The
-//    DMA is issued from inline asm so the compiler does not add its own
-//    whole-queue waits in front of every LDS read.
+//    global_load_lds DMA so in-flight tiles cost no registers.  Every wave
+//    issues a fixed number of DMA instructions per stage (every lane active,
+//    every address valid), so "this wave's share of stage s has landed" is
+//    s_waitcnt vmcnt(n * D) with n the stages it issued after s; a workgroup
+//    barrier after that wait makes the whole stage visible.  The DMA is
+//    issued from inline asm so the compiler does not add its own whole-queue
+//    waits in front of every LDS read.
 //  * Weights and their scales come pre-tiled (moe_prepare.hip): a stage's B
 //    is one contiguous block already in LDS order, so every DMA instruction
-//    moves 1 KiB of contiguous memory.  A chunks are XOR-swizzled in LDS
-//    (chunk ^ ((row >> 1) & 7)), B chunks by the tiling (chunk ^ ((col >> 2)
-//    & 3)), so the MFMA-pattern ds_read_b128s of 16 consecutive rows/columns
-//    hit distinct banks.
+//    moves 1 KiB of contiguous memory, and the columns are permuted so that
+//    each lane's outputs of four 16-column blocks are adjacent in memory:
+//    the epilogues store dwords (FP8) or 8-byte runs (BF16) straight from
+//    the accumulators.  A chunks are XOR-swizzled in LDS (chunk ^ ((row >> 1)
+//    & 7)), B chunks by the tiling (chunk ^ ((col >> 2) & 3)), so the
+//    MFMA-pattern ds_read_b128s of 16 consecutive rows/columns hit distinct
+//    banks.
+//  * 512-column tiles run 8 waves as two groups of four that alternate
+//    ("ping-pong"): while one group issues the MFMAs of its K-step, the other
+//    reads its next fragments from LDS and issues its share of the DMA, and
+//    every phase change is a workgroup barrier.  The two waves sharing a
+//    SIMD are thus never both waiting on LDS, which a single group of
+//    barrier-synchronised waves cannot avoid.  Group 0 streams the weights,
+//    group 1 the activation rows.  256-column tiles (small N) use one group
+//    of four waves that reads, then multiplies.
 //  * Tiles come from a list (expert by expert; for each N-tile all M-tiles
 //    of the expert) and blockIdx is remapped so that each XCD (blockIdx % 8
 //    on MI300-class parts) runs a contiguous run of that list: the M-tiles
@@ -52,6 +60,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kBK = 128;
 constexpr int kTileN = 256;  // width of one tiled-weight block (moe_prepare.hip)
 constexpr int kNumXcd = 8;
+constexpr int kLdsBudget = 155 * 1024;  // operand ring; the rest of the 160 KiB holds per-row tables
 
 struct GemmArgs {
     const uint8_t* a;      // Linear1: x [T, K]; Linear2: h_q [cap, K]
@@ -70,7 +79,7 @@ struct GemmArgs {
 
 __device__ __forceinline__ float bf16_round(float v) { return (float)(__bf16)v; }
 
-__device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+__device__ __forceinline__ uint32_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
 
 // UE8M0 code of the smallest power of two 2^s with amax / 2^s <= 448, from
 // the exponent and mantissa bits (448 = 1.75 * 2^8).
@@ -84,279 +93,457 @@ __device__ __forceinline__ float pow2_neg(int code) {  // 2^(127 - code), code i
     return __uint_as_float((uint32_t)(254 - code) << 23);
 }
 
-// ---- LDS DMA: lane l writes `size` bytes at LDS address m0 + l * size.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+// Cross-lane moves inside a 16-lane row (DPP, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
-    asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+constexpr int kDppRor8 = 0x128;        // lane i <- lane (i + 8) % 16: swaps the two halves of a row
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7 - i within each group of 8
+
+// max over the 8 lanes of each aligned group of 8
+__device__ __forceinline__ float max8(float v) {
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    return fmaxf(v, dpp<kDppHalfMirror>(v));
+}
+
+// ---- LDS DMA: lane l reads `size` bytes at the wave-uniform base plus its
+// own 32-bit offset and writes them at LDS address m0 + l * size.
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, uint32_t lds) {
+    asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 // Wait until at most N DMA instructions of this wave are in flight and this
-// wave's LDS reads are done, then meet the other waves.
+// wave's LDS reads are done, then meet the other waves.  The scheduling
+// barriers keep the compiler from moving MFMAs or LDS reads across it.
 template <int N>
-__device__ __forceinline__ void wait_stage_and_barrier() {
+__device__ __forceinline__ void wait_and_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
 }
+// up to n (0..2) later stages of D instructions each may stay in flight
+template <int D>
+__device__ __forceinline__ void wait_stages_and_barrier(int n) {
+    if (n >= 2) wait_and_barrier<2 * D>();
+    else if (n == 1) wait_and_barrier<D>();
+    else wait_and_barrier<0>();
+}
+constexpr int kNoVmWait = 63;  // vmcnt field maximum: wait for LDS reads only
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
-template <int BM, int BN, int NW>
-struct Cfg {
-    static constexpr int THREADS = 64 * NW;
-    static constexpr int WM = BM >= 128 ? 2 : 1;       // wave grid rows
-    static constexpr int WN = NW / WM;                  // wave grid cols
-    static constexpr int WTM = BM / WM;                 // wave tile rows
-    static constexpr int WTN = BN / WN;                 // wave tile cols
-    static_assert(WTN % 64 == 0, "a wave must own whole 64-column requant groups");
-    static constexpr int MI = WTM / 16;
-    static constexpr int NI = WTN / 16;
+// Tile of this workgroup: XCD-contiguous runs of the tile list.  False for
+// the padding workgroups of the grid.
+struct TileId {
+    int m, n, e;
+};
+__device__ __forceinline__ bool tile_of_block(const GemmArgs& g, int BM, int BN, TileId& t) {
+    const int total = (g.scalars[0] / BM) * (g.N / BN);
+    const int share = (total + kNumXcd - 1) / kNumXcd;
+    const int slot = blockIdx.x / kNumXcd;
+    if (slot >= share) return false;
+    const int L = (blockIdx.x % kNumXcd) * share + slot;
+    if (L >= total) return false;
+    t.m = g.tiles[2 * L];
+    t.n = g.tiles[2 * L + 1] >> 16;
+    t.e = g.tiles[2 * L + 1] & 0xFFFF;
+    return true;
+}
+
+// ---- operand layout of one LDS stage
+template <int BM, int BN>
+struct StageLayout {
     static constexpr int A_BYTES = BM * kBK;
     static constexpr int B_BYTES = BN * (kBK / 2);
     static constexpr int SA_WORDS = BM > 64 ? BM : 64;  // one DMA instruction covers 64 rows
     static constexpr int SB_WORDS = BN;
     static constexpr int STAGE = A_BYTES + B_BYTES + 4 * SA_WORDS + 4 * SB_WORDS;
-    static constexpr int NS = (152 * 1024) / STAGE >= 4 ? 4 : 3;  // LDS stages
-    static constexpr int A_INSTR = A_BYTES / 1024;      // 1 KiB per wave DMA instruction
-    static constexpr int A_PW = A_INSTR >= NW ? A_INSTR / NW : 1;
-    static constexpr int B_PW = B_BYTES / 1024 / NW;
+    static constexpr int NS = kLdsBudget / STAGE >= 4 ? 4 : 3;
+    static_assert(kLdsBudget / STAGE >= 3, "three stages must fit");
+    static constexpr int A_INSTR = A_BYTES / 1024;  // 1 KiB per DMA instruction
+    static constexpr int B_INSTR = B_BYTES / 1024;
     static constexpr int SA_INSTR = SA_WORDS / 64;
     static constexpr int SB_INSTR = SB_WORDS / 64;
-    static constexpr int SB_PW = SB_INSTR >= NW ? SB_INSTR / NW : 1;
-    static constexpr int D_W = A_PW + B_PW + 1 + SB_PW;  // DMA instructions per wave per stage
-    static_assert(A_INSTR % NW == 0 || A_INSTR < NW, "A instructions must split evenly");
-    static_assert((B_BYTES / 1024) % NW == 0, "B instructions must split evenly");
-    static_assert(2 * D_W < 64, "vmcnt range");
 };
 
-template <int BM, int BN, int NW, bool L1>
-struct Smem {
-    using C = Cfg<BM, BN, NW>;
-    static constexpr int kMain = C::NS * C::STAGE;
-    static constexpr int kEpi = L1 ? BM * (BN / 2) : BM * BN * 2;
-    static constexpr int kBytes = (kMain > kEpi ? kMain : kEpi);
+// DMA sources of one wave.  The A side (rows and their scales) is split over
+// `anw` waves, the B side (weights and their scales) over `bnw` waves; where
+// an operand has fewer instructions than waves, waves repeat one, writing
+// the same bytes to the same place.  Bases are wave-uniform (SGPRs); only the
+// per-lane offsets live in VGPRs.
+template <int BM, int BN, int A_PW, int B_PW, int SB_PW>
+struct StageDma {
+    using L = StageLayout<BM, BN>;
+    uint32_t a_off[A_PW];  // gathered row * K + chunk
+    uint32_t sa_off;
+    const uint8_t* a;
+    const uint8_t* a_sf;
+    const uint8_t* b;
+    const uint8_t* b_sf;
+    int KT, aw, anw, bw, bnw, sa_blk;
+
+    // Linear1 gathers rows through row_token; its padding rows read token 0
+    // (their top-k weight is 0, so they produce h = 0)
+    __device__ __forceinline__ void init_a(const GemmArgs& g, int m_tile, const int* row_tok, bool l1, int aw_,
+                                           int anw_, int lane) {
+        aw = aw_; anw = anw_;
+        KT = g.K / kBK;
+#pragma unroll
+        for (int i = 0; i < A_PW; ++i) {
+            const int blk = (i * anw + aw) % L::A_INSTR;
+            const int p = blk * 64 + lane;             // 16-byte LDS slot of this lane
+            const int row = p >> 3;
+            const int c = (p & 7) ^ ((row >> 1) & 7);  // logical chunk stored in that slot
+            int src_row;
+            if (l1) {
+                const int t = row_tok[row];
+                src_row = t >= 0 ? t : 0;
+            } else {
+                src_row = m_tile * BM + row;
+            }
+            a_off[i] = (uint32_t)src_row * (uint32_t)g.K + (uint32_t)(c * 16);
+        }
+        a = g.a;
+        sa_blk = aw % L::SA_INSTR;
+        sa_off = (uint32_t)min(sa_blk * 64 + lane, BM - 1) * 4;
+        a_sf = g.a_sf + (size_t)m_tile * KT * (4 * BM);
+    }
+    __device__ __forceinline__ void init_b(const GemmArgs& g, const TileId& t, int bw_, int bnw_) {
+        bw = bw_; bnw = bnw_;
+        KT = g.K / kBK;
+        const int tn0 = t.n * (BN / kTileN);  // first 256-column block of this tile
+        const size_t tb0 = ((size_t)t.e * (g.N / kTileN) + tn0) * KT;
+        b = g.b + tb0 * 16 * 1024;
+        b_sf = g.b_sf + tb0 * 256 * 4;
+    }
+    __device__ __forceinline__ void issue_a(uint8_t* st, int kt, int lane) const {
+#pragma unroll
+        for (int i = 0; i < A_PW; ++i) {
+            const int blk = (i * anw + aw) % L::A_INSTR;
+            dma16(a_off[i], a + (size_t)kt * kBK, lds_addr(st + blk * 1024));
+        }
+        dma4(sa_off, a_sf + (size_t)kt * (4 * BM), lds_addr(st + L::A_BYTES + L::B_BYTES + sa_blk * 256));
+    }
+    __device__ __forceinline__ void issue_b(uint8_t* st, int kt, int lane) const {
+#pragma unroll
+        for (int i = 0; i < B_PW; ++i) {
+            const int blk = i * bnw + bw;  // 1 KiB block of this stage's B (16 per 256 columns)
+            dma16((uint32_t)lane * 16, b + ((size_t)((blk >> 4) * KT + kt) * 16 + (blk & 15)) * 1024,
+                  lds_addr(st + L::A_BYTES + blk * 1024));
+        }
+#pragma unroll
+        for (int i = 0; i < SB_PW; ++i) {
+            const int blk = (i * bnw + bw) % L::SB_INSTR;  // 64 columns per instruction
+            dma4((uint32_t)lane * 4, b_sf + ((size_t)((blk >> 2) * KT + kt) * 256 + (blk & 3) * 64) * 4,
+                 lds_addr(st + L::A_BYTES + L::B_BYTES + 4 * L::SA_WORDS + blk * 256));
+        }
+    }
 };
 
-template <int BM, int BN, int NW, bool L1>
-__global__ __launch_bounds__(64 * NW, 1) void gemm_kernel(GemmArgs g) {
-    using C = Cfg<BM, BN, NW>;
-    using S = Smem<BM, BN, NW, L1>;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[S::kBytes];
+// ---- fragments of one wave tile (MI x NI MFMA blocks) for one K-step
+template <int MI, int NI>
+struct Frags {
+    v8i a[MI];
+    v4i b[NI];
+    int sa[MI], sb[NI];
+};
+
+template <int BM, int BN, int MI, int NI>
+__device__ __forceinline__ void read_frags(Frags<MI, NI>& f, const uint8_t* st, int wrow0, int wcol0, int lane) {
+    using L = StageLayout<BM, BN>;
+    const int gq = lane >> 4;
+    const uint8_t* A = st;
+    const uint8_t* Bt = st + L::A_BYTES;
+    const uint32_t* SA = reinterpret_cast<const uint32_t*>(st + L::A_BYTES + L::B_BYTES);
+    const uint32_t* SB = SA + L::SA_WORDS;
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+        const int col = wcol0 + ni * 16 + (lane & 15);
+        f.b[ni] = *reinterpret_cast<const v4i*>(Bt + col * (kBK / 2) + ((gq ^ ((col >> 2) & 3)) << 4));
+        f.sb[ni] = (int)(SB[col] >> (8 * gq));
+    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+        const int row = wrow0 + mi * 16 + (lane & 15);
+        const int sw = (row >> 1) & 7;
+        const v4i lo = *reinterpret_cast<const v4i*>(A + row * kBK + ((gq ^ sw) << 4));
+        const v4i hi = *reinterpret_cast<const v4i*>(A + row * kBK + (((4 + gq) ^ sw) << 4));
+        f.a[mi] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        f.sa[mi] = (int)(SA[row] >> (8 * gq));
+    }
+}
+
+template <int MI, int NI>
+__device__ __forceinline__ void mfma_step(v4f (&acc)[MI][NI], const Frags<MI, NI>& f) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+            const v8i b = v8i{f.b[ni][0], f.b[ni][1], f.b[ni][2], f.b[ni][3], 0, 0, 0, 0};
+            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.a[mi], b, acc[mi][ni], 0, 4, 0,
+                                                                            f.sa[mi], 0, f.sb[ni]);
+        }
+}
+
+// ---- epilogues: straight from the accumulators to global memory.
+// wrow0: the wave's first row within the tile; gcol0: its first global output
+// column (a multiple of 64).  The weight tiling permutes columns so that, in
+// a 64-column group, MFMA block b = ni % 4 gives lane l the output
+// 4*(l & 7) + b of the group's 32 SwiGLU channels (Linear1, gate in lanes
+// l & 8 == 0, up in the others) or 4*(l & 15) + b of its 64 columns (Linear2).
+template <int BM, int MI, int NI>
+__device__ __forceinline__ void epilogue_linear1(const v4f (&acc)[MI][NI], const GemmArgs& g, int m_tile, int wrow0,
+                                                 int gcol0, const float* row_w, int lane) {
+    static_assert(NI % 4 == 0, "a wave owns whole 64-column groups");
+    const bool gate_lane = (lane & 8) == 0;
+    const int j8 = lane & 7;
+    const int n_q = g.N / 2;
+    const int ksteps2 = g.N / kTileN;  // Linear2 K-steps (128 channels each)
+    constexpr float kLog2e = 1.4426950408889634f;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+        for (int grp = 0; grp < NI / 4; ++grp) {
+            const int gcol = gcol0 + grp * 64;  // first Z column of this 32-channel group
+            // lanes j and j + 8 hold the gate and the up row of one channel: swap halves
+            float other[4][4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) other[b][i] = dpp<kDppRor8>(acc[mi][grp * 4 + b][i]);
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+                // gate lanes finish rows 0-1 of the lane's four, up lanes rows 2-3
+                const int row_local = wrow0 + mi * 16 + 4 * (lane >> 4) + (gate_lane ? ii : 2 + ii);
+                const float wgt = row_w[row_local];
+                float h[4];
+                float amax = 0.0f;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const float gv = bf16_round(gate_lane ? acc[mi][grp * 4 + b][ii] : other[b][2 + ii]);
+                    const float uv = bf16_round(gate_lane ? other[b][ii] : acc[mi][grp * 4 + b][2 + ii]);
+                    // silu(g) = g / (1 + 2^(-g log2 e)) with the hardware exp2 and reciprocal
+                    const float s = gv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv * kLog2e));
+                    h[b] = (s * uv) * wgt;
+                    amax = fmaxf(amax, fabsf(h[b]));
+                }
+                amax = max8(amax);
+                const int code = requant_code(amax);
+                const float inv = pow2_neg(code);
+                int q = __builtin_amdgcn_cvt_pk_fp8_f32(h[0] * inv, h[1] * inv, 0, false);
+                q = __builtin_amdgcn_cvt_pk_fp8_f32(h[2] * inv, h[3] * inv, q, true);
+                const size_t row = (size_t)m_tile * BM + row_local;
+                *reinterpret_cast<int*>(g.out_q + row * n_q + gcol / 2 + 4 * j8) = q;
+                // Linear2 K-step = 256-column block of Z, byte = 64-column group within it
+                if (j8 == 0)
+                    g.out_sf[(((size_t)m_tile * ksteps2 + gcol / kTileN) * BM + row_local) * 4 + (gcol % kTileN) / 64] =
+                        (uint8_t)code;
+            }
+        }
+    }
+}
+
+template <int BM, int MI, int NI>
+__device__ __forceinline__ void epilogue_linear2(const v4f (&acc)[MI][NI], const GemmArgs& g, int m_tile, int wrow0,
+                                                 int gcol0, const int* row_tok, int lane) {
+    static_assert(NI % 4 == 0, "a wave owns whole 64-column groups");
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row_local = wrow0 + mi * 16 + 4 * (lane >> 4) + i;
+            if (row_tok[row_local] < 0) continue;  // padding rows are never read
+            uint16_t* out = g.out_bf16 + ((size_t)m_tile * BM + row_local) * g.N + gcol0 + 4 * (lane & 15);
+#pragma unroll
+            for (int grp = 0; grp < NI / 4; ++grp) {
+                const uint32_t lo = bf16_bits(acc[mi][grp * 4 + 0][i]) | (bf16_bits(acc[mi][grp * 4 + 1][i]) << 16);
+                const uint32_t hi = bf16_bits(acc[mi][grp * 4 + 2][i]) | (bf16_bits(acc[mi][grp * 4 + 3][i]) << 16);
+                *reinterpret_cast<uint2*>(out + grp * 64) = uint2{lo, hi};
+            }
+        }
+}
+
+template <int BM, int MI, int NI, bool L1>
+__device__ __forceinline__ void epilogue(const v4f (&acc)[MI][NI], const GemmArgs& g, int m_tile, int wrow0,
+                                         int gcol0, const float* row_w, const int* row_tok, int lane) {
+    if constexpr (L1) epilogue_linear1<BM>(acc, g, m_tile, wrow0, gcol0, row_w, lane);
+    else epilogue_linear2<BM>(acc, g, m_tile, wrow0, gcol0, row_tok, lane);
+}
+
+template <int BM, bool L1>
+__device__ __forceinline__ void load_row_tables(const GemmArgs& g, int m_tile, float* row_w, int* row_tok, int tid) {
+    if (tid < BM) {
+        row_tok[tid] = g.row_token[m_tile * BM + tid];
+        if (L1) row_w[tid] = g.row_w[m_tile * BM + tid];
+    }
+    __syncthreads();
+}
+
+template <int MI, int NI>
+__device__ __forceinline__ void zero(v4f (&acc)[MI][NI]) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
+}
+
+// ============================================================================
+// 256-column tiles: one group of 4 waves; per K-step wait, read, multiply.
+template <int BM>
+struct Cfg4 {
+    using L = StageLayout<BM, 256>;
+    static constexpr int WM = BM >= 128 ? 2 : 1;  // wave grid rows
+    static constexpr int WN = 4 / WM;
+    static constexpr int WTM = BM / WM;
+    static constexpr int WTN = 256 / WN;
+    static_assert(WTN % 64 == 0, "a wave must own whole 64-column requant groups");
+    static constexpr int MI = WTM / 16, NI = WTN / 16;
+    static constexpr int A_PW = L::A_INSTR >= 4 ? L::A_INSTR / 4 : 1;
+    static constexpr int B_PW = L::B_INSTR / 4;
+    static constexpr int SB_PW = L::SB_INSTR / 4;
+    static constexpr int D = A_PW + 1 + B_PW + SB_PW;  // DMA instructions per wave per stage
+    static_assert(2 * D < 64, "vmcnt range");
+};
+
+template <int BM, bool L1>
+__global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
+    using C = Cfg4<BM>;
+    using L = typename C::L;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[L::NS * L::STAGE];
     __shared__ float row_w[BM];
     __shared__ int row_tok[BM];
 
-    // ---- tile of this workgroup (XCD-contiguous runs of the tile list)
-    const int nt = g.N / BN;
-    const int total = (g.scalars[0] / BM) * nt;
-    const int share = (total + kNumXcd - 1) / kNumXcd;
-    const int slot = blockIdx.x / kNumXcd;
-    if (slot >= share) return;
-    const int L = (blockIdx.x % kNumXcd) * share + slot;
-    if (L >= total) return;
-    const int m_tile = g.tiles[2 * L];
-    const int n_tile = g.tiles[2 * L + 1] >> 16;
-    const int e = g.tiles[2 * L + 1] & 0xFFFF;
+    TileId t;
+    if (!tile_of_block(g, BM, 256, t)) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int KT = g.K / kBK;
+    load_row_tables<BM, L1>(g, t.m, row_w, row_tok, tid);
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int r0 = m_tile * BM;
-    const int K = g.K, N = g.N;
-    const int KT = K / kBK;
-
-    if (tid < BM) {
-        row_tok[tid] = g.row_token[r0 + tid];
-        if (L1) row_w[tid] = g.row_w[r0 + tid];
-    }
-    __syncthreads();
-
-    // ---- per-lane DMA sources
-    uint32_t a_off[C::A_PW];
-#pragma unroll
-    for (int i = 0; i < C::A_PW; ++i) {
-        const int blk = (i * NW + w) % C::A_INSTR;
-        const int p = blk * 64 + lane;             // 16-byte LDS slot of this lane
-        const int row = p >> 3;
-        const int c = (p & 7) ^ ((row >> 1) & 7);  // logical chunk stored in that slot
-        int src_row;
-        if (L1) {
-            const int t = row_tok[row];
-            src_row = t >= 0 ? t : 0;              // padding rows read token 0 (their weight is 0)
-        } else {
-            src_row = r0 + row;
-        }
-        a_off[i] = (uint32_t)src_row * (uint32_t)K + (uint32_t)(c * 16);
-    }
-    // tiled weights: stage kt of one 256-column block is 16 KiB (+1 KiB of scales), contiguous
-    const int tn0 = n_tile * (BN / kTileN);  // first 256-column block of this tile
-    const size_t tb0 = ((size_t)e * (N / kTileN) + tn0) * KT;
-    const uint8_t* a_base = g.a;
-    const int sa_blk = w % C::SA_INSTR;
-    const uint8_t* a_sf_base = g.a_sf + (size_t)m_tile * KT * (4 * BM) + min(sa_blk * 64 + lane, BM - 1) * 4;
-
-    auto issue_stage = [&](int kt) {
-        uint8_t* st = smem + (kt % C::NS) * C::STAGE;
-#pragma unroll
-        for (int i = 0; i < C::A_PW; ++i) {
-            const int blk = (i * NW + w) % C::A_INSTR;
-            dma16(a_base + a_off[i] + (uint32_t)kt * kBK, lds_addr(st + blk * 1024));
-        }
-#pragma unroll
-        for (int i = 0; i < C::B_PW; ++i) {
-            const int blk = i * NW + w;          // 1 KiB block of this stage's B (16 per 256 columns)
-            const uint8_t* src = g.b + ((tb0 + (size_t)(blk >> 4) * KT + kt) * 16 + (blk & 15)) * 1024 + lane * 16;
-            dma16(src, lds_addr(st + C::A_BYTES + blk * 1024));
-        }
-        dma4(a_sf_base + (size_t)kt * (4 * BM), lds_addr(st + C::A_BYTES + C::B_BYTES + sa_blk * 256));
-#pragma unroll
-        for (int i = 0; i < C::SB_PW; ++i) {
-            const int blk = (i * NW + w) % C::SB_INSTR;  // 64 columns per instruction
-            const uint8_t* src = g.b_sf + ((tb0 + (size_t)(blk >> 2) * KT + kt) * 256 + (blk & 3) * 64 + lane) * 4;
-            dma4(src, lds_addr(st + C::A_BYTES + C::B_BYTES + 4 * C::SA_WORDS + blk * 256));
-        }
+    StageDma<BM, 256, C::A_PW, C::B_PW, C::SB_PW> dma;
+    dma.init_a(g, t.m, row_tok, L1, w, 4, lane);
+    dma.init_b(g, t, w, 4);
+    auto issue = [&](int kt) {
+        uint8_t* st = smem + (kt % L::NS) * L::STAGE;
+        dma.issue_a(st, kt, lane);
+        dma.issue_b(st, kt, lane);
     };
 
-    const int wm = w / C::WN, wn = w % C::WN;
-    const int gq = lane >> 4;
+    const int wrow0 = (w / C::WN) * C::WTM, wcol0 = (w % C::WN) * C::WTN;
     v4f acc[C::MI][C::NI];
+    zero(acc);
 #pragma unroll
-    for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-    for (int s = 0; s < C::NS - 1; ++s)
-        if (s < KT) issue_stage(s);
-
+    for (int s = 0; s < L::NS - 1; ++s)
+        if (s < KT) issue(s);
     for (int kt = 0; kt < KT; ++kt) {
-        const int after = min(C::NS - 2, KT - 1 - kt);  // stages issued after kt
-        if (after >= 2) wait_stage_and_barrier<2 * C::D_W>();
-        else if (after == 1) wait_stage_and_barrier<C::D_W>();
-        else wait_stage_and_barrier<0>();
-        if (kt + C::NS - 1 < KT) issue_stage(kt + C::NS - 1);
-
-        const uint8_t* st = smem + (kt % C::NS) * C::STAGE;
-        const uint8_t* A = st;
-        const uint8_t* Bt = st + C::A_BYTES;
-        const uint32_t* SA = reinterpret_cast<const uint32_t*>(st + C::A_BYTES + C::B_BYTES);
-        const uint32_t* SB = SA + C::SA_WORDS;
-        v8i bfrag[C::NI];
-        int sb[C::NI];
-#pragma unroll
-        for (int ni = 0; ni < C::NI; ++ni) {
-            const int col = wn * C::WTN + ni * 16 + (lane & 15);
-            const v4i b = *reinterpret_cast<const v4i*>(Bt + col * (kBK / 2) + ((gq ^ ((col >> 2) & 3)) << 4));
-            bfrag[ni] = v8i{b[0], b[1], b[2], b[3], 0, 0, 0, 0};
-            sb[ni] = (int)(SB[col] >> (8 * gq));
-        }
-#pragma unroll
-        for (int mi = 0; mi < C::MI; ++mi) {
-            const int row = wm * C::WTM + mi * 16 + (lane & 15);
-            const int sw = (row >> 1) & 7;
-            const v4i lo = *reinterpret_cast<const v4i*>(A + row * kBK + ((gq ^ sw) << 4));
-            const v4i hi = *reinterpret_cast<const v4i*>(A + row * kBK + (((4 + gq) ^ sw) << 4));
-            const v8i afrag = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            const int sa = (int)(SA[row] >> (8 * gq));
-#pragma unroll
-            for (int ni = 0; ni < C::NI; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afrag, bfrag[ni], acc[mi][ni], 0, 4,
-                                                                                0, sa, 0, sb[ni]);
-        }
+        wait_stages_and_barrier<C::D>(min(L::NS - 2, KT - 1 - kt));  // stage kt landed; kt-1 fully read
+        if (kt + L::NS - 1 < KT) issue(kt + L::NS - 1);
+        Frags<C::MI, C::NI> f;
+        read_frags<BM, 256>(f, smem + (kt % L::NS) * L::STAGE, wrow0, wcol0, lane);
+        mfma_step(acc, f);
     }
-    __syncthreads();  // every wave is done with the stages before they are reused below
+    epilogue<BM, C::MI, C::NI, L1>(acc, g, t.m, wrow0, t.n * 256 + wcol0, row_w, row_tok, lane);
+}
 
-    if constexpr (L1) {
-        // ---- SwiGLU x w -> amax -> UE8M0 -> FP8, staged through LDS
-        uint8_t* stage = smem;  // [BM][BN/2] channel bytes of this tile
-        const bool gate_lane = (lane & 8) == 0;
-        const int ksteps2 = N / kTileN;  // Linear2 K-steps (128 channels each)
+// ============================================================================
+// 512-column tiles: two groups of 4 waves in ping-pong.
+//
+// Phases are separated by workgroup barriers B_0, B_1, ...  Group 0 reads
+// stage kt in phase 2kt and multiplies it in phase 2kt+1; group 1 reads it
+// in phase 2kt+1 and multiplies it in phase 2kt+2.  Stage kt is therefore
+// read between B_2kt and B_2kt+2, so:
+//   * before B_2kt each wave waits for its own share of stage kt (vmcnt);
+//   * stage kt + NS - 1 reuses the buffer of stage kt - 1, which is free
+//     after B_2kt; group 0 issues its share in phase 2kt, group 1 in 2kt+1;
+//   * a wave finishing a read phase waits for its LDS reads (lgkmcnt(0))
+//     before the barrier, so the buffer it read may be refilled after it.
+// Both groups pass the same 2*KT barriers (group 1 skips B_2KT, which would
+// only separate its last reads from its last MFMAs).
+template <int BM>
+struct CfgPP {
+    using L = StageLayout<BM, 512>;
+    static constexpr bool SPLIT_ROWS = BM == 128;  // the groups split the rows, else the columns
+    static constexpr int WTM = SPLIT_ROWS ? 64 : BM;
+    static constexpr int WTN = SPLIT_ROWS ? 128 : 64;
+    static constexpr int MI = WTM / 16, NI = WTN / 16;
+    static constexpr int B_PW = L::B_INSTR / 4;  // group 0: weights and their scales
+    static constexpr int SB_PW = L::SB_INSTR / 4;
+    static constexpr int D0 = B_PW + SB_PW;
+    static constexpr int A_PW = L::A_INSTR >= 4 ? L::A_INSTR / 4 : 1;  // group 1: rows and their scales
+    static constexpr int D1 = A_PW + 1;
+    static_assert(2 * D0 < kNoVmWait && 2 * D1 < kNoVmWait, "vmcnt range");
+};
+
+template <int BM, bool L1>
+__global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
+    using C = CfgPP<BM>;
+    using L = typename C::L;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[L::NS * L::STAGE];
+    __shared__ float row_w[BM];
+    __shared__ int row_tok[BM];
+
+    TileId t;
+    if (!tile_of_block(g, BM, 512, t)) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = w >> 2, wq = w & 3;
+    const int KT = g.K / kBK;
+    load_row_tables<BM, L1>(g, t.m, row_w, row_tok, tid);
+
+    const int wrow0 = C::SPLIT_ROWS ? grp * C::WTM : 0;
+    const int wcol0 = C::SPLIT_ROWS ? wq * C::WTN : grp * 256 + wq * C::WTN;
+    v4f acc[C::MI][C::NI];
+    zero(acc);
+
+    if (grp == 0) {
+        StageDma<BM, 512, 1, C::B_PW, C::SB_PW> dma;
+        dma.init_b(g, t, wq, 4);
+        auto issue = [&](int kt) { dma.issue_b(smem + (kt % L::NS) * L::STAGE, kt, lane); };
 #pragma unroll
-        for (int mi = 0; mi < C::MI; ++mi) {
-            v4f other[C::NI];
-#pragma unroll
-            for (int ni = 0; ni < C::NI; ++ni)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) other[ni][c] = __shfl_xor(acc[mi][ni][c], 8, 64);
-#pragma unroll
-            for (int grp = 0; grp < C::NI / 4; ++grp) {  // 64 columns = 32 channels = one scale group
-                const int col0 = wn * C::WTN + grp * 64;  // first column of the group in this tile
-                const int ch0 = col0 / 2 + (lane & 7);
-#pragma unroll
-                for (int ii = 0; ii < 2; ++ii) {
-                    const int i = gate_lane ? ii : 2 + ii;
-                    const int row_local = wm * C::WTM + mi * 16 + 4 * (lane >> 4) + i;
-                    const float wgt = row_w[row_local];
-                    float h[4];
-                    float amax = 0.0f;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int ni = grp * 4 + q;
-                        const float zg = gate_lane ? acc[mi][ni][i] : other[ni][i];
-                        const float zu = gate_lane ? other[ni][i] : acc[mi][ni][i];
-                        const float gv = bf16_round(zg);
-                        const float uv = bf16_round(zu);
-                        const float s = gv / (1.0f + expf(-gv));
-                        h[q] = (s * uv) * wgt;
-                        amax = fmaxf(amax, fabsf(h[q]));
-                    }
-                    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-                    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-                    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
-                    const int code = requant_code(amax);
-                    const float inv = pow2_neg(code);
-                    const int q01 = __builtin_amdgcn_cvt_pk_fp8_f32(h[0] * inv, h[1] * inv, 0, false);
-                    const int q23 = __builtin_amdgcn_cvt_pk_fp8_f32(h[2] * inv, h[3] * inv, 0, false);
-                    uint8_t* srow = stage + row_local * (BN / 2) + ch0;
-                    srow[0] = (uint8_t)(q01 & 0xFF);
-                    srow[8] = (uint8_t)((q01 >> 8) & 0xFF);
-                    srow[16] = (uint8_t)(q23 & 0xFF);
-                    srow[24] = (uint8_t)((q23 >> 8) & 0xFF);
-                    // Linear2 K-step = 256-column block of this tile's Z, byte = group within it
-                    if ((lane & 7) == 0) {
-                        const int gcol = n_tile * BN + col0;
-                        g.out_sf[(((size_t)m_tile * ksteps2 + gcol / kTileN) * BM + row_local) * 4 +
-                                 (gcol % kTileN) / 64] = (uint8_t)code;
-                    }
-                }
-            }
-        }
-        __syncthreads();
-        const int n_q = N / 2;
-        constexpr int CPR = BN / 32;  // 16-byte chunks per staged row
-        for (int c = tid; c < BM * CPR; c += C::THREADS) {
-            const int row = c / CPR, ch = c % CPR;
-            *reinterpret_cast<v4i*>(g.out_q + (size_t)(r0 + row) * n_q + n_tile * (BN / 2) + ch * 16) =
-                *reinterpret_cast<const v4i*>(stage + row * (BN / 2) + ch * 16);
+        for (int s = 0; s < L::NS - 1; ++s)
+            if (s < KT) issue(s);
+        for (int kt = 0; kt < KT; ++kt) {
+            wait_stages_and_barrier<C::D0>(min(L::NS - 2, KT - 1 - kt));  // B_2kt
+            if (kt + L::NS - 1 < KT) issue(kt + L::NS - 1);
+            Frags<C::MI, C::NI> f;
+            read_frags<BM, 512>(f, smem + (kt % L::NS) * L::STAGE, wrow0, wcol0, lane);
+            wait_and_barrier<kNoVmWait>();                                 // B_2kt+1
+            mfma_step(acc, f);
         }
     } else {
-        // ---- FP32 -> BF16, staged through LDS, padding rows skipped
-        uint16_t* stage = reinterpret_cast<uint16_t*>(smem);  // [BM][BN]
+        StageDma<BM, 512, C::A_PW, 1, 1> dma;
+        dma.init_a(g, t.m, row_tok, L1, wq, 4, lane);
+        auto issue = [&](int kt) { dma.issue_a(smem + (kt % L::NS) * L::STAGE, kt, lane); };
 #pragma unroll
-        for (int mi = 0; mi < C::MI; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < C::NI; ++ni)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row_local = wm * C::WTM + mi * 16 + 4 * (lane >> 4) + i;
-                    const int col_local = wn * C::WTN + ni * 16 + (lane & 15);
-                    stage[row_local * BN + col_local] = bf16_bits(acc[mi][ni][i]);
-                }
-        __syncthreads();
-        constexpr int CPR = BN / 8;
-        for (int c = tid; c < BM * CPR; c += C::THREADS) {
-            const int row = c / CPR, ch = c % CPR;
-            if (row_tok[row] < 0) continue;
-            *reinterpret_cast<v4i*>(g.out_bf16 + (size_t)(r0 + row) * N + n_tile * BN + ch * 8) =
-                *reinterpret_cast<const v4i*>(stage + row * BN + ch * 8);
+        for (int s = 0; s < L::NS - 1; ++s)
+            if (s < KT) issue(s);
+        wait_stages_and_barrier<C::D1>(min(L::NS - 2, KT - 1));            // B_0
+        for (int kt = 0; kt < KT; ++kt) {
+            wait_and_barrier<kNoVmWait>();                                 // B_2kt+1
+            if (kt + L::NS - 1 < KT) issue(kt + L::NS - 1);
+            Frags<C::MI, C::NI> f;
+            read_frags<BM, 512>(f, smem + (kt % L::NS) * L::STAGE, wrow0, wcol0, lane);
+            if (kt + 1 < KT) wait_stages_and_barrier<C::D1>(min(L::NS - 2, KT - 2 - kt));  // B_2kt+2
+            mfma_step(acc, f);
         }
     }
+    epilogue<BM, C::MI, C::NI, L1>(acc, g, t.m, wrow0, t.n * 512 + wcol0, row_w, row_tok, lane);
 }
 
 template <int BM, bool L1>
 hipError_t launch_bm(const GemmArgs& args, int64_t grid, hipStream_t stream) {
     if (gemm_bn(args.N) == 512)
-        hipLaunchKernelGGL((gemm_kernel<BM, 512, 8, L1>), dim3(grid), dim3(512), 0, stream, args);
+        hipLaunchKernelGGL((gemm_pp_kernel<BM, L1>), dim3(grid), dim3(512), 0, stream, args);
     else
-        hipLaunchKernelGGL((gemm_kernel<BM, 256, 4, L1>), dim3(grid), dim3(256), 0, stream, args);
+        hipLaunchKernelGGL((gemm4_kernel<BM, L1>), dim3(grid), dim3(256), 0, stream, args);
     return hipGetLastError();
 }
 

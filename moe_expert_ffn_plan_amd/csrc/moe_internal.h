@@ -114,8 +114,8 @@ hipError_t launch_linear1(const GemmProblem& g, const uint8_t* x, const uint8_t*
                           hipStream_t stream);
 hipError_t launch_linear2(const GemmProblem& g, const uint8_t* h_q, const uint8_t* h_sf, const uint8_t* w2,
                           const uint8_t* w2_sf, uint16_t* yslot, hipStream_t stream);
-hipError_t launch_tile_weights(int N, int K, int E, const uint8_t* w, const uint8_t* w_sf, uint8_t* w_out,
-                               uint8_t* sf_out, hipStream_t stream);
+hipError_t launch_tile_weights(int which, int N, int K, int E, const uint8_t* w, const uint8_t* w_sf,
+                               uint8_t* w_out, uint8_t* sf_out, hipStream_t stream);
 hipError_t launch_prep_linear1(const moe_shape& s, const uint8_t* x_sf, const float* topk_w, const PlanPtrs& p,
                                int64_t cap, int nt1, int nt2, uint32_t* xsf_out, float* row_w, int32_t* tiles1,
                                int32_t* tiles2, hipStream_t stream);

@@ -13,6 +13,18 @@
 //   scales [E][N/256][K/128][256 columns][4 B]: the four UE8M0 bytes of the
 //          column for that K-step.
 //
+// Tile column c of a 256-column block holds weight row nt*256 + src(c).  The
+// permutation is chosen for the GEMM epilogues: an MFMA output lane owns one
+// column of each 16-column block, so within every 64-column group the
+// columns are ordered so that one lane's four blocks hold four adjacent
+// outputs (c = 64G + 16b + j, b = 0..3, j = 0..15):
+//   Linear1 (N = 2I, rows interleaved gate/up by 8): lanes j < 8 hold the
+//     gate and lanes j + 8 the up row of channel 32G + 4(j & 7) + b, so the
+//     two halves of a 16-lane row pair up and a lane ends with four adjacent
+//     FP8 outputs (one dword);
+//   Linear2 (N = H): column 64G + 4j + b, so a lane owns four adjacent BF16
+//     outputs (8 bytes).
+//
 // The activation-side scales get the analogous per-row-block layout
 //   [R/BM][K/128][BM rows][4 B]
 // (prep_linear1_kernel builds it for Linear1's gathered rows; the Linear1
@@ -25,8 +37,19 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void tile_weight_data_kernel(const uint8_t* __restrict__ w, int N, int K,
-                                                                    int64_t n_slots, uint8_t* __restrict__ out) {
+// Weight row (within its 256-row block) stored at tile column c.
+__device__ __forceinline__ int tile_source_col(int which, int c) {
+    const int G = c >> 6, b = (c >> 4) & 3, j = c & 15;
+    if (which == 1) {
+        const int ch = G * 32 + (j & 7) * 4 + b;           // SwiGLU channel within the block
+        return (ch >> 3) * 16 + (ch & 7) + (j & 8);        // its gate (j < 8) or up row
+    }
+    return G * 64 + j * 4 + b;
+}
+
+__global__ __launch_bounds__(kThreads) void tile_weight_data_kernel(const uint8_t* __restrict__ w, int which, int N,
+                                                                    int K, int64_t n_slots,
+                                                                    uint8_t* __restrict__ out) {
     const int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // output slot
     if (s >= n_slots) return;
     const int KT = K / 128, NT = N / 256;
@@ -38,13 +61,14 @@ __global__ __launch_bounds__(kThreads) void tile_weight_data_kernel(const uint8_
     const int64_t e = blk / NT;
     const int c = p >> 2;
     const int q = (p & 3) ^ ((c >> 2) & 3);
-    const int64_t col = (int64_t)nt * 256 + c;
+    const int64_t col = (int64_t)nt * 256 + tile_source_col(which, c);
     const uint8_t* src = w + (e * N + col) * (K / 2) + (int64_t)kt * 64 + q * 16;
     *reinterpret_cast<v4i*>(out + s * 16) = *reinterpret_cast<const v4i*>(src);
 }
 
-__global__ __launch_bounds__(kThreads) void tile_weight_scale_kernel(const uint8_t* __restrict__ sf, int N, int K,
-                                                                     int64_t n_words, uint32_t* __restrict__ out) {
+__global__ __launch_bounds__(kThreads) void tile_weight_scale_kernel(const uint8_t* __restrict__ sf, int which, int N,
+                                                                     int K, int64_t n_words,
+                                                                     uint32_t* __restrict__ out) {
     const int64_t s = (int64_t)blockIdx.x * kThreads + threadIdx.x;  // output word
     if (s >= n_words) return;
     const int KT = K / 128, NT = N / 256;
@@ -54,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void tile_weight_scale_kernel(const uint8
     blk /= KT;
     const int nt = (int)(blk % NT);
     const int64_t e = blk / NT;
-    const int64_t col = (int64_t)nt * 256 + c;
+    const int64_t col = (int64_t)nt * 256 + tile_source_col(which, c);
     out[s] = *reinterpret_cast<const uint32_t*>(sf + (e * N + col) * (K / 32) + (int64_t)kt * 4);
 }
 
@@ -112,16 +136,17 @@ __global__ __launch_bounds__(kThreads) void prep_linear1_kernel(const uint8_t* _
 
 }  // namespace
 
-hipError_t launch_tile_weights(int N, int K, int E, const uint8_t* w, const uint8_t* w_sf, uint8_t* w_out,
-                               uint8_t* sf_out, hipStream_t stream) {
+hipError_t launch_tile_weights(int which, int N, int K, int E, const uint8_t* w, const uint8_t* w_sf,
+                               uint8_t* w_out, uint8_t* sf_out, hipStream_t stream) {
     const int64_t slots = (int64_t)E * N * K / 32;      // 16-byte slots = E*N*(K/2)/16
     const int64_t words = (int64_t)E * N * K / 128;
     if (slots > 0)
         hipLaunchKernelGGL(tile_weight_data_kernel, dim3((unsigned)((slots + kThreads - 1) / kThreads)),
-                           dim3(kThreads), 0, stream, w, N, K, slots, w_out);
+                           dim3(kThreads), 0, stream, w, which, N, K, slots, w_out);
     if (words > 0)
         hipLaunchKernelGGL(tile_weight_scale_kernel, dim3((unsigned)((words + kThreads - 1) / kThreads)),
-                           dim3(kThreads), 0, stream, w_sf, N, K, words, reinterpret_cast<uint32_t*>(sf_out));
+                           dim3(kThreads), 0, stream, w_sf, which, N, K, words,
+                           reinterpret_cast<uint32_t*>(sf_out));
     return hipGetLastError();
 }
 

@@ -97,17 +97,29 @@ def test_forward_tp_slice_full(gpu):
     check_full(w, {k: v.cpu() for k, v in d.items()}, out)
 
 
-def _tile_reference(w, w_sf, N, K):
+def _tile_columns(which):
+    """Weight row (within a 256-row block) stored at each tile column, as documented in moe.h."""
+    c = np.arange(256)
+    G, b, j = c >> 6, (c >> 4) & 3, c & 15
+    if which == 1:
+        ch = 32 * G + 4 * (j & 7) + b                  # SwiGLU channel; gate rows for j < 8, up rows for j >= 8
+        return (ch // 8) * 16 + (ch % 8) + 8 * (j >= 8)
+    return 64 * G + 4 * j + b
+
+
+def _tile_reference(w, w_sf, N, K, which):
     """The documented tiled layout, built with NumPy index arithmetic."""
     E = w.shape[0]
     NT, KT = N // 256, K // 128
+    src = _tile_columns(which)
+    assert np.array_equal(np.sort(src), np.arange(256))
     p = np.arange(1024)
     c = p >> 2
     q = (p & 3) ^ ((c >> 2) & 3)
-    chunks = w.reshape(E, NT, 256, KT, 4, 16)                       # [e, nt, col, kt, chunk, 16]
+    chunks = w.reshape(E, NT, 256, KT, 4, 16)[:, :, src]            # [e, nt, tile col, kt, chunk, 16]
     data = chunks[:, :, c, :, q, :]                                  # [1024, e, nt, kt, 16] (advanced dims first)
     data = np.moveaxis(data, 0, 3).reshape(-1)                       # [e, nt, kt, 1024, 16]
-    sf = w_sf.reshape(E, NT, 256, KT, 4).transpose(0, 1, 3, 2, 4).reshape(-1)
+    sf = w_sf.reshape(E, NT, 256, KT, 4)[:, :, src].transpose(0, 1, 3, 2, 4).reshape(-1)
     return data, sf
 
 
@@ -120,7 +132,7 @@ def test_prepare_weights_layout(gpu, which):
     N, K = (2 * w.intermediate, w.hidden) if which == 1 else (w.hidden, w.intermediate)
     wt, sft = B.prepare_weights(s, which, d[key].to(gpu), d[key + "_sf"].to(gpu))
     torch.cuda.synchronize()
-    want_w, want_sf = _tile_reference(d[key].numpy(), d[key + "_sf"].numpy(), N, K)
+    want_w, want_sf = _tile_reference(d[key].numpy(), d[key + "_sf"].numpy(), N, K, which)
     assert np.array_equal(wt.cpu().numpy(), want_w)
     assert np.array_equal(sft.cpu().numpy(), want_sf)
 
