@@ -65,6 +65,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--host-inputs", action="store_true",
                     help="draw the synthetic inputs on the CPU and copy them (fewer torch GPU kernels, for profilers)")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run a plain elementwise copy (y = -x, float32) of this many MiB five times: the "
+                         "reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs one GPU's share of the MoE layer; --gpus {args.gpus} is not supported "
@@ -79,6 +82,15 @@ def main() -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     dev = torch.device("cuda:0")
+    if args.copy_mb:
+        n = args.copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "dispatches": 5}), flush=True)
+        return 0
     w = inputs.WORKLOADS[args.workload]
     s = B.shape_of(w)
     gen_dev = "cpu" if args.host_inputs else dev

@@ -161,7 +161,7 @@ MOE_API int moe_forward_workspace_bytes(const moe_shape* shape, size_t* bytes);
  * E*N*K/2 bytes, w_sf_tiled E*N*K/32):
  *   w_tiled    [E][N/256][K/128][1024 slots of 16 B]: slot p holds bytes
  *              [kt*64 + q*16, +16) of tile column c = p >> 2, with
- *              q = (p & 3) ^ ((c >> 2) & 3);
+ *              q = (p & 3) ^ ((c >> 1) & 3);
  *   w_sf_tiled [E][N/256][K/128][256 columns][4 B]: the column's four
  *              scale bytes for that K-step;
  *   tile column c of block nt (c = 64G + 16b + j, b < 4, j < 16) holds

@@ -33,9 +33,12 @@
 //    each lane's outputs of four 16-column blocks are adjacent in memory:
 //    the epilogues store dwords (FP8) or 8-byte runs (BF16) straight from
 //    the accumulators.  A chunks are XOR-swizzled in LDS (chunk ^ ((row >> 1)
-//    & 7)), B chunks by the tiling (chunk ^ ((col >> 2) & 3)), so the
-//    MFMA-pattern ds_read_b128s of 16 consecutive rows/columns hit distinct
-//    banks.
+//    & 7)), B chunks by the tiling (chunk ^ ((col >> 1) & 3)).  Measured on
+//    the device, a ds_read_b128 runs without bank conflicts when the lanes
+//    l, l^2, l^4, l^6 of each group address distinct 16-byte slots modulo
+//    128 bytes; both swizzles give that for the MFMA fragment reads of 16
+//    consecutive rows or columns (with chunk ^ ((col >> 2) & 3) the B reads
+//    were two-way conflicted).
 //  * 512-column tiles run 8 waves as two groups of four that alternate
 //    ("ping-pong"): while one group issues the MFMAs of its K-step, the other
 //    reads its next fragments from LDS and issues its share of the DMA, and
@@ -49,6 +52,9 @@
 //    on MI300-class parts) runs a contiguous run of that list: the M-tiles
 //    sharing a weight tile run together on one XCD and hit its L2.
 #include "moe_internal.h"
+
+#include <algorithm>
+#include <atomic>
 
 namespace moe {
 namespace {
@@ -267,7 +273,7 @@ __device__ __forceinline__ void read_frags(Frags<MI, NI>& f, const uint8_t* st, 
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
         const int col = wcol0 + ni * 16 + (lane & 15);
-        f.b[ni] = *reinterpret_cast<const v4i*>(Bt + col * (kBK / 2) + ((gq ^ ((col >> 2) & 3)) << 4));
+        f.b[ni] = *reinterpret_cast<const v4i*>(Bt + col * (kBK / 2) + ((gq ^ ((col >> 1) & 3)) << 4));
         f.sb[ni] = (int)(SB[col] >> (8 * gq));
     }
 #pragma unroll
@@ -340,12 +346,13 @@ __device__ __forceinline__ void epilogue_linear1(const v4f (&acc)[MI][NI], const
                 const float inv = pow2_neg(code);
                 int q = __builtin_amdgcn_cvt_pk_fp8_f32(h[0] * inv, h[1] * inv, 0, false);
                 q = __builtin_amdgcn_cvt_pk_fp8_f32(h[2] * inv, h[3] * inv, q, true);
-                const size_t row = (size_t)m_tile * BM + row_local;
-                *reinterpret_cast<int*>(g.out_q + row * n_q + gcol / 2 + 4 * j8) = q;
+                // 32-bit offsets from uniform bases (cap * I < 2^31 is checked on the host)
+                const uint32_t row = (uint32_t)(m_tile * BM + row_local);
+                *reinterpret_cast<int*>(g.out_q + (row * (uint32_t)n_q + (uint32_t)(gcol / 2 + 4 * j8))) = q;
                 // Linear2 K-step = 256-column block of Z, byte = 64-column group within it
                 if (j8 == 0)
-                    g.out_sf[(((size_t)m_tile * ksteps2 + gcol / kTileN) * BM + row_local) * 4 + (gcol % kTileN) / 64] =
-                        (uint8_t)code;
+                    g.out_sf[(((uint32_t)(m_tile * ksteps2 + gcol / kTileN) * BM + row_local) * 4 +
+                              (uint32_t)((gcol % kTileN) / 64))] = (uint8_t)code;
             }
         }
     }
@@ -361,12 +368,15 @@ __device__ __forceinline__ void epilogue_linear2(const v4f (&acc)[MI][NI], const
         for (int i = 0; i < 4; ++i) {
             const int row_local = wrow0 + mi * 16 + 4 * (lane >> 4) + i;
             if (row_tok[row_local] < 0) continue;  // padding rows are never read
-            uint16_t* out = g.out_bf16 + ((size_t)m_tile * BM + row_local) * g.N + gcol0 + 4 * (lane & 15);
+            // 32-bit byte offsets from a uniform base (cap * H * 2 < 2^32)
+            const uint32_t off = ((uint32_t)(m_tile * BM + row_local) * (uint32_t)g.N +
+                                  (uint32_t)(gcol0 + 4 * (lane & 15))) * 2u;
+            uint8_t* out = reinterpret_cast<uint8_t*>(g.out_bf16);
 #pragma unroll
             for (int grp = 0; grp < NI / 4; ++grp) {
                 const uint32_t lo = bf16_bits(acc[mi][grp * 4 + 0][i]) | (bf16_bits(acc[mi][grp * 4 + 1][i]) << 16);
                 const uint32_t hi = bf16_bits(acc[mi][grp * 4 + 2][i]) | (bf16_bits(acc[mi][grp * 4 + 3][i]) << 16);
-                *reinterpret_cast<uint2*>(out + grp * 64) = uint2{lo, hi};
+                *reinterpret_cast<uint2*>(out + (off + (uint32_t)(grp * 128))) = uint2{lo, hi};
             }
         }
 }
@@ -454,19 +464,37 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
 }
 
 // ============================================================================
-// 512-column tiles: two groups of 4 waves in ping-pong.
+// 512-column tiles: two groups of 4 waves in ping-pong, persistent over a
+// run of tiles.
+//
+// A workgroup owns tiles L_j = first + j * nslots (j < ntiles) of its XCD's
+// contiguous chunk of the tile list and walks their K-steps as one sequence
+// gs = 0 .. S-1 (S = ntiles * KT; tile j = gs / KT, K-step gs % KT), so the
+// operand ring runs on across tile boundaries and the next tile's first
+// stages load while the current one finishes.
 //
 // Phases are separated by workgroup barriers B_0, B_1, ...  Group 0 reads
-// stage kt in phase 2kt and multiplies it in phase 2kt+1; group 1 reads it
-// in phase 2kt+1 and multiplies it in phase 2kt+2.  Stage kt is therefore
-// read between B_2kt and B_2kt+2, so:
-//   * before B_2kt each wave waits for its own share of stage kt (vmcnt);
-//   * stage kt + NS - 1 reuses the buffer of stage kt - 1, which is free
-//     after B_2kt; group 0 issues its share in phase 2kt, group 1 in 2kt+1;
+// stage gs in phase 2gs and multiplies it in phase 2gs+1; group 1 reads it
+// in phase 2gs+1 and multiplies it in phase 2gs+2.  Stage gs is therefore
+// read between B_2gs and B_2gs+2, so:
+//   * before B_2gs each wave waits for its own share of stage gs (vmcnt);
+//   * stage gs + NS - 1 reuses the buffer of stage gs - 1, which is free
+//     after B_2gs; group 0 issues its share in phase 2gs, group 1 in 2gs+1;
 //   * a wave finishing a read phase waits for its LDS reads (lgkmcnt(0))
 //     before the barrier, so the buffer it read may be refilled after it.
-// Both groups pass the same 2*KT barriers (group 1 skips B_2KT, which would
-// only separate its last reads from its last MFMAs).
+// Both groups pass the same 2*S barriers (group 1 skips B_2S, which would
+// only separate its last reads from its last MFMAs).  A group runs the
+// epilogue of a tile right after its last MFMA phase of that tile.
+//
+// Per-tile tables reach LDS through the same DMA stream, one extra
+// instruction per wave per stage so the vmcnt arithmetic stays exact:
+// group 0 loads the list entry of tile ci + 2 into desc[(ci + 2) % 3] and
+// group 1 the row tokens and top-k weights of tile ci + 1 into meta[(ci + 1)
+// % 3] (ci = the tile being multiplied; between tile changes the same load
+// repeats, rewriting identical bytes).  With KT >= 2 (NS - 1) K-steps per
+// tile every table has landed before it is read: a list entry by the time
+// its rows are fetched, the rows by the time the tile's first stage is
+// issued.  Below that the kernel runs one tile per workgroup.
 template <int BM>
 struct CfgPP {
     using L = StageLayout<BM, 512>;
@@ -474,90 +502,189 @@ struct CfgPP {
     static constexpr int WTM = SPLIT_ROWS ? 64 : BM;
     static constexpr int WTN = SPLIT_ROWS ? 128 : 64;
     static constexpr int MI = WTM / 16, NI = WTN / 16;
-    static constexpr int B_PW = L::B_INSTR / 4;  // group 0: weights and their scales
+    static constexpr int B_PW = L::B_INSTR / 4;  // group 0: weights and their scales, + list entry
     static constexpr int SB_PW = L::SB_INSTR / 4;
-    static constexpr int D0 = B_PW + SB_PW;
-    static constexpr int A_PW = L::A_INSTR >= 4 ? L::A_INSTR / 4 : 1;  // group 1: rows and their scales
-    static constexpr int D1 = A_PW + 1;
+    static constexpr int D0 = B_PW + SB_PW + 1;
+    static constexpr int A_PW = L::A_INSTR >= 4 ? L::A_INSTR / 4 : 1;  // group 1: rows, scales, + row tables
+    static constexpr int D1 = A_PW + 1 + 1;
+    static constexpr int MIN_KT_PERSISTENT = 2 * (L::NS - 1);
     static_assert(2 * D0 < kNoVmWait && 2 * D1 < kNoVmWait, "vmcnt range");
+    static_assert(BM <= 128, "row tables hold 128 rows");
 };
+constexpr int kTableSlots = 3;
 
 template <int BM, bool L1>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
     using C = CfgPP<BM>;
     using L = typename C::L;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[L::NS * L::STAGE];
-    __shared__ float row_w[BM];
-    __shared__ int row_tok[BM];
+    __shared__ int desc[kTableSlots][64];   // words 0, 1: the tile's list entry {m, n << 16 | e}
+    __shared__ int meta[kTableSlots][256];  // [0, 128): row tokens; [128, 256): top-k weights (Linear1)
 
-    TileId t;
-    if (!tile_of_block(g, BM, 512, t)) return;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int grp = w >> 2, wq = w & 3;
     const int KT = g.K / kBK;
-    load_row_tables<BM, L1>(g, t.m, row_w, row_tok, tid);
+
+    // ---- this workgroup's tiles
+    const int total = (g.scalars[0] / BM) * (g.N / 512);
+    const int share = (total + kNumXcd - 1) / kNumXcd;
+    const int nslots = gridDim.x / kNumXcd;
+    const int xcd = blockIdx.x % kNumXcd;
+    const int first = xcd * share + blockIdx.x / kNumXcd;
+    const int end = min((xcd + 1) * share, total);
+    if (first >= end) return;
+    const int ntiles = (end - first + nslots - 1) / nslots;
+    const int S = ntiles * KT;
+    auto tile_entry = [&](int j) { return g.tiles + 2 * (first + min(j, ntiles - 1) * nslots); };
+
+    // ---- table loads (one DMA instruction per wave)
+    auto load_desc = [&](int j) {  // group 0
+        j = min(j, ntiles - 1);
+        dma4((uint32_t)min(lane, 1) * 4, tile_entry(j), lds_addr(&desc[j % kTableSlots][0]));
+    };
+    auto load_meta = [&](int j, int m) {  // group 1; m = M-tile of tile j
+        j = min(j, ntiles - 1);
+        const int part = wq >> 1, half = wq & 1;
+        const int row = min(half * 64 + lane, BM - 1);
+        const void* src = (L1 && part == 1) ? static_cast<const void*>(g.row_w + (size_t)m * BM)
+                                            : static_cast<const void*>(g.row_token + (size_t)m * BM);
+        dma4((uint32_t)row * 4, src, lds_addr(&meta[j % kTableSlots][part * 128 + half * 64]));
+    };
+    auto read_entry = [&](int j, TileId& t) {
+        j = min(j, ntiles - 1);
+        const int a = __builtin_amdgcn_readfirstlane(desc[j % kTableSlots][0]);
+        const int b = __builtin_amdgcn_readfirstlane(desc[j % kTableSlots][1]);
+        t.m = a; t.n = b >> 16; t.e = b & 0xFFFF;
+    };
 
     const int wrow0 = C::SPLIT_ROWS ? grp * C::WTM : 0;
     const int wcol0 = C::SPLIT_ROWS ? wq * C::WTN : grp * 256 + wq * C::WTN;
     v4f acc[C::MI][C::NI];
     zero(acc);
+    TileId ct;  // tile being multiplied
+
+    // ---- prologue: list entries of tiles 0 and 1, then the rows of tile 0
+    if (grp == 0) load_desc(wq & 1);
+    wait_and_barrier<0>();
+    TileId t0;
+    read_entry(0, t0);
+    if (grp == 1) load_meta(0, t0.m);
+    wait_and_barrier<0>();
 
     if (grp == 0) {
         StageDma<BM, 512, 1, C::B_PW, C::SB_PW> dma;
-        dma.init_b(g, t, wq, 4);
-        auto issue = [&](int kt) { dma.issue_b(smem + (kt % L::NS) * L::STAGE, kt, lane); };
+        dma.init_b(g, t0, wq, 4);
+        // stage s (and the table load that rides with it) for compute step gs = s - (NS - 1)
+        auto issue = [&](int s) {
+            if (s % KT == 0 && s > 0) {
+                TileId t;
+                read_entry(s / KT, t);
+                dma.init_b(g, t, wq, 4);
+            }
+            dma.issue_b(smem + (s % L::NS) * L::STAGE, s % KT, lane);
+            load_desc(max(s - (L::NS - 1), 0) / KT + 2);
+        };
 #pragma unroll
         for (int s = 0; s < L::NS - 1; ++s)
-            if (s < KT) issue(s);
-        for (int kt = 0; kt < KT; ++kt) {
-            wait_stages_and_barrier<C::D0>(min(L::NS - 2, KT - 1 - kt));  // B_2kt
-            if (kt + L::NS - 1 < KT) issue(kt + L::NS - 1);
+            if (s < S) issue(s);
+        for (int gs = 0, kt = 0, ci = 0; gs < S; ++gs) {
+            wait_stages_and_barrier<C::D0>(min(L::NS - 2, S - 1 - gs));  // B_2gs
+            if (kt == 0) read_entry(ci, ct);
+            if (gs + L::NS - 1 < S) issue(gs + L::NS - 1);
             Frags<C::MI, C::NI> f;
-            read_frags<BM, 512>(f, smem + (kt % L::NS) * L::STAGE, wrow0, wcol0, lane);
-            wait_and_barrier<kNoVmWait>();                                 // B_2kt+1
+            read_frags<BM, 512>(f, smem + (gs % L::NS) * L::STAGE, wrow0, wcol0, lane);
+            wait_and_barrier<kNoVmWait>();                                 // B_2gs+1
             mfma_step(acc, f);
+            if (++kt == KT) {
+                const int* mt = meta[ci % kTableSlots];
+                epilogue<BM, C::MI, C::NI, L1>(acc, g, ct.m, wrow0, ct.n * 512 + wcol0,
+                                               reinterpret_cast<const float*>(mt + 128), mt, lane);
+                zero(acc);
+                kt = 0;
+                ++ci;
+            }
         }
     } else {
         StageDma<BM, 512, C::A_PW, 1, 1> dma;
-        dma.init_a(g, t.m, row_tok, L1, wq, 4, lane);
-        auto issue = [&](int kt) { dma.issue_a(smem + (kt % L::NS) * L::STAGE, kt, lane); };
+        dma.init_a(g, t0.m, meta[0], L1, wq, 4, lane);
+        TileId tn;  // tile whose rows the table load fetches
+        read_entry(1, tn);
+        auto issue = [&](int s) {
+            if (s % KT == 0 && s > 0) {
+                TileId t;
+                read_entry(s / KT, t);
+                dma.init_a(g, t.m, meta[(s / KT) % kTableSlots], L1, wq, 4, lane);
+            }
+            dma.issue_a(smem + (s % L::NS) * L::STAGE, s % KT, lane);
+            load_meta(max(s - (L::NS - 1), 0) / KT + 1, tn.m);
+        };
 #pragma unroll
         for (int s = 0; s < L::NS - 1; ++s)
-            if (s < KT) issue(s);
-        wait_stages_and_barrier<C::D1>(min(L::NS - 2, KT - 1));            // B_0
-        for (int kt = 0; kt < KT; ++kt) {
-            wait_and_barrier<kNoVmWait>();                                 // B_2kt+1
-            if (kt + L::NS - 1 < KT) issue(kt + L::NS - 1);
+            if (s < S) issue(s);
+        wait_stages_and_barrier<C::D1>(min(L::NS - 2, S - 1));             // B_0
+        for (int gs = 0, kt = 0, ci = 0; gs < S; ++gs) {
+            wait_and_barrier<kNoVmWait>();                                 // B_2gs+1
+            if (kt == 0) {
+                read_entry(ci, ct);
+                read_entry(ci + 1, tn);
+            }
+            if (gs + L::NS - 1 < S) issue(gs + L::NS - 1);
             Frags<C::MI, C::NI> f;
-            read_frags<BM, 512>(f, smem + (kt % L::NS) * L::STAGE, wrow0, wcol0, lane);
-            if (kt + 1 < KT) wait_stages_and_barrier<C::D1>(min(L::NS - 2, KT - 2 - kt));  // B_2kt+2
+            read_frags<BM, 512>(f, smem + (gs % L::NS) * L::STAGE, wrow0, wcol0, lane);
+            if (gs + 1 < S) wait_stages_and_barrier<C::D1>(min(L::NS - 2, S - 2 - gs));  // B_2gs+2
             mfma_step(acc, f);
+            if (++kt == KT) {
+                const int* mt = meta[ci % kTableSlots];
+                epilogue<BM, C::MI, C::NI, L1>(acc, g, ct.m, wrow0, ct.n * 512 + wcol0,
+                                               reinterpret_cast<const float*>(mt + 128), mt, lane);
+                zero(acc);
+                kt = 0;
+                ++ci;
+            }
         }
     }
-    epilogue<BM, C::MI, C::NI, L1>(acc, g, t.m, wrow0, t.n * 512 + wcol0, row_w, row_tok, lane);
+}
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+        cache[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
 }
 
 template <int BM, bool L1>
-hipError_t launch_bm(const GemmArgs& args, int64_t grid, hipStream_t stream) {
-    if (gemm_bn(args.N) == 512)
+hipError_t launch_bm(const GemmArgs& args, int64_t tiles, hipStream_t stream) {
+    const int64_t all = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;  // one workgroup per tile
+    if (gemm_bn(args.N) == 512) {
+        int64_t grid = all;
+        if (args.K / kBK >= CfgPP<BM>::MIN_KT_PERSISTENT) {  // persistent: one workgroup per CU
+            const int64_t cus = cu_count() / kNumXcd * kNumXcd;
+            grid = std::max<int64_t>(kNumXcd, std::min(all, cus));
+        }
         hipLaunchKernelGGL((gemm_pp_kernel<BM, L1>), dim3(grid), dim3(512), 0, stream, args);
-    else
-        hipLaunchKernelGGL((gemm4_kernel<BM, L1>), dim3(grid), dim3(256), 0, stream, args);
+    } else {
+        hipLaunchKernelGGL((gemm4_kernel<BM, L1>), dim3(all), dim3(256), 0, stream, args);
+    }
     return hipGetLastError();
 }
 
 template <bool L1>
 hipError_t launch_gemm(const GemmProblem& p, const GemmArgs& args, hipStream_t stream) {
     const int bm = p.shape->block_m;
-    const int64_t tiles = (p.cap / bm) * (args.N / gemm_bn(args.N));
-    const int64_t grid = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
-    if (grid == 0) return hipSuccess;
+    const int64_t tiles = (p.cap / bm) * (args.N / gemm_bn(args.N));  // upper bound (padded rows not yet known)
+    if (tiles == 0) return hipSuccess;
     switch (bm) {
-        case 16: return launch_bm<16, L1>(args, grid, stream);
-        case 32: return launch_bm<32, L1>(args, grid, stream);
-        case 64: return launch_bm<64, L1>(args, grid, stream);
-        case 128: return launch_bm<128, L1>(args, grid, stream);
+        case 16: return launch_bm<16, L1>(args, tiles, stream);
+        case 32: return launch_bm<32, L1>(args, tiles, stream);
+        case 64: return launch_bm<64, L1>(args, tiles, stream);
+        case 128: return launch_bm<128, L1>(args, tiles, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -8,7 +8,7 @@
 // the stage loads are fully contiguous 1 KiB DMA transfers:
 //
 //   data   [E][N/256][K/128][1024 slots of 16 B]; slot p holds the 16 bytes
-//          of tile column c = p >> 2, logical chunk q = (p & 3) ^ ((c >> 2) & 3),
+//          of tile column c = p >> 2, logical chunk q = (p & 3) ^ ((c >> 1) & 3),
 //          i.e. bytes [kt*64 + q*16, +16) of that column's packed FP4 row;
 //   scales [E][N/256][K/128][256 columns][4 B]: the four UE8M0 bytes of the
 //          column for that K-step.
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void tile_weight_data_kernel(const uint8_
     const int nt = (int)(blk % NT);
     const int64_t e = blk / NT;
     const int c = p >> 2;
-    const int q = (p & 3) ^ ((c >> 2) & 3);
+    const int q = (p & 3) ^ ((c >> 1) & 3);
     const int64_t col = (int64_t)nt * 256 + tile_source_col(which, c);
     const uint8_t* src = w + (e * N + col) * (K / 2) + (int64_t)kt * 64 + q * 16;
     *reinterpret_cast<v4i*>(out + s * 16) = *reinterpret_cast<const v4i*>(src);

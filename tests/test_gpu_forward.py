@@ -115,7 +115,7 @@ def _tile_reference(w, w_sf, N, K, which):
     assert np.array_equal(np.sort(src), np.arange(256))
     p = np.arange(1024)
     c = p >> 2
-    q = (p & 3) ^ ((c >> 2) & 3)
+    q = (p & 3) ^ ((c >> 1) & 3)
     chunks = w.reshape(E, NT, 256, KT, 4, 16)[:, :, src]            # [e, nt, tile col, kt, chunk, 16]
     data = chunks[:, :, c, :, q, :]                                  # [1024, e, nt, kt, 16] (advanced dims first)
     data = np.moveaxis(data, 0, 3).reshape(-1)                       # [e, nt, kt, 1024, 16]
