@@ -7,14 +7,17 @@ One step = the whole hot path on one batch of synthetic input already resident
 in HBM: routing tables (moe_plan), grouped Linear1 with the fused
 SwiGLU/requant epilogue, grouped Linear2, and the top-k combine, enqueued on
 one stream.  The four stages are the same calls moe_forward makes; they are
-issued one by one so HIP events on that stream can time each kernel.  Three
-copies of the expert weights are rotated between steps so they stream from
-HBM rather than the 256 MB Infinity Cache.
+issued one by one so HIP events on that stream can bracket the Linear1 kernel
+inside the timed steps (the roofline's achieved rate).  Three copies of the
+expert weights are rotated between steps so they stream from HBM rather than
+the 256 MB Infinity Cache.  The default warmup (50 steps) lets the clocks
+settle; the first steps after idle run ~15% slower.
 
 Prints one JSON line with the metric (useful TFLOP/s = 2 * N_valid * 3 * H * I
-per step, the reading notes' FLOP count), tokens/s, the roofline of the
-dominant kernel measured with HIP events, and the CPU oracle timed on a
-bounded sample of the same workload.
+per step, the reading notes' FLOP count, over the wall time of the timed
+steps), tokens/s, the roofline of the dominant kernel, per-stage kernel times
+from a separate untimed pass with an event between every stage, and the CPU
+oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -32,36 +35,40 @@ PEAK_MFMA_TFLOPS = 5000.0      # MI355X dense FP8 MFMA; FP8 x FP4 scaled MFMA is
 PEAK_HBM_GBS = 8000.0
 
 
-def cpu_baseline(w, d_gpu, sample_tokens: int):
-    """Time the CPU oracle (untuned) on the first `sample_tokens` tokens of the workload."""
+def cpu_baseline(w, d_gpu, sample_tokens: int, min_seconds: float = 10.0):
+    """Time the CPU oracle (untuned) on the first `sample_tokens` tokens of the workload, repeated until
+    at least `min_seconds` have passed."""
     import numpy as np
     from moe_expert_ffn_plan_amd import inputs
     from oracle.forward import forward_tokens
     d = inputs.to_numpy(d_gpu)
     toks = np.arange(min(sample_tokens, w.num_tokens))
-    t0 = time.perf_counter()
-    _, hits = forward_tokens(toks, d["x"], d["x_sf"], d["topk_idx"], d["topk_w"], d["w1"], d["w1_sf"], d["w2"],
-                             d["w2_sf"], num_experts=w.num_experts, expert_begin=0)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * len(hits) * 3 * w.hidden * w.intermediate
+    reps, dt = 0, 0.0
+    while dt < min_seconds:
+        t0 = time.perf_counter()
+        _, hits = forward_tokens(toks, d["x"], d["x_sf"], d["topk_idx"], d["topk_w"], d["w1"], d["w1_sf"],
+                                 d["w2"], d["w2_sf"], num_experts=w.num_experts, expert_begin=0)
+        dt += time.perf_counter() - t0
+        reps += 1
+    flops = 2.0 * len(hits) * 3 * w.hidden * w.intermediate * reps
     try:
         from threadpoolctl import threadpool_info
         cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) or 1
     except Exception:
         cores = os.cpu_count() or 1
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {toks.size} tokens ({len(hits)} local top-k rows), whole oracle forward incl. "
-                      f"weight dequantisation, {dt:.1f} s"}
+            "sample": f"first {toks.size} of {w.num_tokens} tokens ({len(hits)} local top-k rows), whole oracle "
+                      f"forward incl. weight dequantisation, {reps} run(s), {dt:.1f} s"}
 
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="tp_slice")
     ap.add_argument("--weight-copies", type=int, default=3)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=384)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--host-inputs", action="store_true",
                     help="draw the synthetic inputs on the CPU and copy them (fewer torch GPU kernels, for profilers)")
@@ -108,13 +115,17 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     stages = ["plan", "linear1", "linear2", "combine"]
 
-    def step(i, events=None):
+    def step(i, events=None, l1_events=None):
         wt = weights[i % len(weights)]
         rec = (lambda j: events[j].record(stream)) if events is not None else (lambda j: None)
         rec(0)
         B.plan(s, d["topk_idx"], plan_ws, stream)
         rec(1)
+        if l1_events is not None:
+            l1_events[0].record(stream)
         B.linear1(s, d["x"], d["x_sf"], d["topk_w"], wt["w1"], wt["w1_sf"], plan_ws, ws, stream)
+        if l1_events is not None:
+            l1_events[1].record(stream)
         rec(2)
         B.linear2(s, wt["w2"], wt["w2_sf"], plan_ws, ws, stream)
         rec(3)
@@ -127,22 +138,31 @@ def main() -> int:
     scal = B.plan_view(s, plan_ws)["scalars"].cpu().tolist()
     r_pad, n_valid = scal[0], scal[2]
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # timed steps: wall time; HIP events bracket only the Linear1 kernel (same stream)
+    l1_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i, l1_events=l1_evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
+    l1_ms = sum(e[0].elapsed_time(e[1]) for e in l1_evs) / args.steps
+
+    # untimed breakdown pass: an event between every stage
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     kern_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, name in enumerate(stages)}
 
     H, I = w.hidden, w.intermediate
     useful = 2.0 * n_valid * 3 * H * I
     tflops = useful / (ms * 1e-3) / 1e12
     l1_flops = 2.0 * n_valid * 2 * I * H
-    l1_tflops = l1_flops / (kern_ms["linear1"] * 1e-3) / 1e12
-    roofline = {"kernel": "linear1 (gemm_kernel<BM, true>)", "bound": "mfma", "achieved": round(l1_tflops, 2),
+    l1_tflops = l1_flops / (l1_ms * 1e-3) / 1e12
+    kname = ("gemm_pp_kernel<%d, true>" if (2 * I) % 512 == 0 else "gemm4_kernel<%d, true>") % w.block_m
+    roofline = {"kernel": f"Linear1 grouped GEMM ({kname})", "bound": "mfma", "achieved": round(l1_tflops, 2),
                 "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(l1_tflops / PEAK_MFMA_TFLOPS, 4),
                 "traffic": None}
     out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -153,6 +173,7 @@ def main() -> int:
                       "valid_rows": n_valid, "padded_rows": r_pad, "weight_copies": args.weight_copies},
            "tokens_per_s": round(w.num_tokens / (ms * 1e-3), 1),
            "pct_of_mfma_peak": round(100 * tflops / PEAK_MFMA_TFLOPS, 2),
+           "linear1_ms": round(l1_ms, 4),
            "kernel_ms": {k: round(v, 4) for k, v in kern_ms.items()},
            "roofline": roofline}
     if not args.no_cpu_baseline:

@@ -94,8 +94,10 @@ MOE_API int moe_capacity_rows(const moe_shape* shape, int64_t* rows);
 MOE_API int moe_plan_workspace_bytes(const moe_shape* shape, size_t* bytes);
 
 /* Build the routing tables of topk_idx (int64 [T, k], global expert ids)
- * into plan_ws (>= moe_plan_workspace_bytes, 256-byte aligned).  One kernel
- * launch; nothing to initialise beforehand. */
+ * into plan_ws (>= moe_plan_workspace_bytes, 256-byte aligned), together
+ * with the two grouped GEMMs' tile lists, which depend on the routing only.
+ * One kernel launch (three for more than 4096 hits); nothing to initialise
+ * beforehand. */
 MOE_API int moe_plan(const moe_shape* shape, const int64_t* topk_idx,
              void* plan_ws, size_t plan_ws_bytes, void* stream);
 
@@ -184,7 +186,8 @@ MOE_API int moe_forward(const moe_shape* shape,
                 const void* plan_ws,
                 void* ws, size_t ws_bytes, void* stream);
 
-/* ---- the forward's stages, one kernel each ---------------------------------
+/* ---- the forward's stages, one kernel each (Linear1 gathers its rows, their
+ * scales and the top-k weights through the plan's row tables itself) -------
  * moe_forward(plan_ws != NULL) is exactly moe_linear1, moe_linear2 and
  * moe_combine in this order on one stream; they are exposed so a caller can
  * schedule or time the stages itself.  Arguments mean what they mean for

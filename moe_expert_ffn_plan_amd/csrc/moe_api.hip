@@ -169,19 +169,9 @@ int moe_linear1(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, c
     if ((st = check_arch_current()) != MOE_OK) return st;
     const PlanPtrs p = plan_ptrs(F.plan, const_cast<void*>(plan_ws));
     char* base = static_cast<char*>(ws);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const int nt1 = 2 * shape->intermediate / gemm_bn(2 * shape->intermediate);
-    const int nt2 = shape->hidden / gemm_bn(shape->hidden);
-    uint32_t* x_sf_tiled = reinterpret_cast<uint32_t*>(base + F.x_sf);
-    float* row_w = reinterpret_cast<float*>(base + F.row_w);
-    int32_t* tiles1 = reinterpret_cast<int32_t*>(base + F.tiles1);
-    int32_t* tiles2 = reinterpret_cast<int32_t*>(base + F.tiles2);
-    hipError_t e = launch_prep_linear1(*shape, x_sf, topk_w, p, F.plan.cap, nt1, nt2, x_sf_tiled, row_w, tiles1,
-                                       tiles2, s);
-    const GemmProblem g{shape, &p, F.plan.cap, tiles1, row_w};
-    if (e == hipSuccess)
-        e = launch_linear1(g, x, reinterpret_cast<const uint8_t*>(x_sf_tiled), w1, w1_sf,
-                           reinterpret_cast<uint8_t*>(base + F.h_q), reinterpret_cast<uint8_t*>(base + F.h_sf), s);
+    const GemmProblem g{shape, &p, F.plan.cap};
+    const hipError_t e = launch_linear1(g, x, x_sf, topk_w, w1, w1_sf, reinterpret_cast<uint8_t*>(base + F.h_q),
+                                        reinterpret_cast<uint8_t*>(base + F.h_sf), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -198,7 +188,7 @@ int moe_linear2(const moe_shape* shape, const uint8_t* w2, const uint8_t* w2_sf,
     if ((st = check_arch_current()) != MOE_OK) return st;
     const PlanPtrs p = plan_ptrs(F.plan, const_cast<void*>(plan_ws));
     char* base = static_cast<char*>(ws);
-    const GemmProblem g{shape, &p, F.plan.cap, reinterpret_cast<const int32_t*>(base + F.tiles2), nullptr};
+    const GemmProblem g{shape, &p, F.plan.cap};
     const hipError_t e = launch_linear2(g, reinterpret_cast<uint8_t*>(base + F.h_q),
                                         reinterpret_cast<uint8_t*>(base + F.h_sf), w2, w2_sf,
                                         reinterpret_cast<uint16_t*>(base + F.yslot), static_cast<hipStream_t>(stream));

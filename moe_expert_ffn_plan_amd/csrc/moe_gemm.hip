@@ -69,18 +69,19 @@ constexpr int kNumXcd = 8;
 constexpr int kLdsBudget = 155 * 1024;  // operand ring; the rest of the 160 KiB holds per-row tables
 
 struct GemmArgs {
-    const uint8_t* a;      // Linear1: x [T, K]; Linear2: h_q [cap, K]
-    const uint8_t* a_sf;   // per-row-block scales [cap/BM][K/128][BM][4]
-    const uint8_t* b;      // tiled weights [E][N/256][K/128][1024 x 16 B]
-    const uint8_t* b_sf;   // tiled weight scales [E][N/256][K/128][256][4]
+    const uint8_t* a;       // Linear1: x [T, K]; Linear2: h_q [cap, K]
+    const uint8_t* a_sf;    // Linear1: x_sf [T, K/32]; Linear2: per-row-block scales [cap/BM][K/128][BM][4]
+    const uint8_t* b;       // tiled weights [E][N/256][K/128][1024 x 16 B]
+    const uint8_t* b_sf;    // tiled weight scales [E][N/256][K/128][256][4]
     const int32_t* scalars;
-    const int32_t* tiles;  // {m_tile, n_tile << 16 | e} per tile
+    const int32_t* tiles;   // {m_tile, n_tile << 16 | e} per tile
     const int32_t* row_token;
-    const float* row_w;    // Linear1: per-row top-k weight
-    uint8_t* out_q;        // Linear1: [cap, N/2]
-    uint8_t* out_sf;       // Linear1: per-row-block scales [cap/BM][N/256][BM][4]
-    uint16_t* out_bf16;    // Linear2: [cap, N]
-    int K, N;
+    const int32_t* row_topk;
+    const float* topk_w;    // Linear1: top-k weights [T, k]
+    uint8_t* out_q;         // Linear1: [cap, N/2]
+    uint8_t* out_sf;        // Linear1: per-row-block scales [cap/BM][N/256][BM][4]
+    uint16_t* out_bf16;     // Linear2: [cap, N]
+    int K, N, topk;
 };
 
 __device__ __forceinline__ float bf16_round(float v) { return (float)(__bf16)v; }
@@ -133,12 +134,19 @@ __device__ __forceinline__ void wait_and_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
     __builtin_amdgcn_sched_barrier(0);
 }
-// up to n (0..2) later stages of D instructions each may stay in flight
+// up to n (0..2) later stages of D instructions each, plus `extra` (0 or 1)
+// further instructions issued with them, may stay in flight
 template <int D>
-__device__ __forceinline__ void wait_stages_and_barrier(int n) {
-    if (n >= 2) wait_and_barrier<2 * D>();
-    else if (n == 1) wait_and_barrier<D>();
-    else wait_and_barrier<0>();
+__device__ __forceinline__ void wait_stages_and_barrier(int n, int extra = 0) {
+    if (n >= 2) {
+        if (extra) wait_and_barrier<2 * D + 1>();
+        else wait_and_barrier<2 * D>();
+    } else if (n == 1) {
+        if (extra) wait_and_barrier<D + 1>();
+        else wait_and_barrier<D>();
+    } else {
+        wait_and_barrier<0>();
+    }
 }
 constexpr int kNoVmWait = 63;  // vmcnt field maximum: wait for LDS reads only
 
@@ -189,15 +197,15 @@ template <int BM, int BN, int A_PW, int B_PW, int SB_PW>
 struct StageDma {
     using L = StageLayout<BM, BN>;
     uint32_t a_off[A_PW];  // gathered row * K + chunk
-    uint32_t sa_off;
+    uint32_t sa_off;       // Linear1: gathered row * K/32; Linear2: row * 4 in the row block
     const uint8_t* a;
     const uint8_t* a_sf;
     const uint8_t* b;
     const uint8_t* b_sf;
-    int KT, aw, anw, bw, bnw, sa_blk;
+    int KT, aw, anw, bw, bnw, sa_blk, sa_kt;
 
-    // Linear1 gathers rows through row_token; its padding rows read token 0
-    // (their top-k weight is 0, so they produce h = 0)
+    // Linear1 gathers rows and their scales through row_token; its padding
+    // rows read token 0 (their top-k weight is 0, so they produce h = 0)
     __device__ __forceinline__ void init_a(const GemmArgs& g, int m_tile, const int* row_tok, bool l1, int aw_,
                                            int anw_, int lane) {
         aw = aw_; anw = anw_;
@@ -219,8 +227,17 @@ struct StageDma {
         }
         a = g.a;
         sa_blk = aw % L::SA_INSTR;
-        sa_off = (uint32_t)min(sa_blk * 64 + lane, BM - 1) * 4;
-        a_sf = g.a_sf + (size_t)m_tile * KT * (4 * BM);
+        const int sa_row = min(sa_blk * 64 + lane, BM - 1);
+        if (l1) {  // x_sf [T, K/32]: the 4 bytes of K-step kt of token t sit at t * K/32 + 4 kt
+            const int t = row_tok[sa_row];
+            sa_off = (uint32_t)(t >= 0 ? t : 0) * (uint32_t)(g.K / 32);
+            a_sf = g.a_sf;
+            sa_kt = 4;
+        } else {   // per-row-block layout [cap/BM][KT][BM][4]
+            sa_off = (uint32_t)sa_row * 4;
+            a_sf = g.a_sf + (size_t)m_tile * KT * (4 * BM);
+            sa_kt = 4 * BM;
+        }
     }
     __device__ __forceinline__ void init_b(const GemmArgs& g, const TileId& t, int bw_, int bnw_) {
         bw = bw_; bnw = bnw_;
@@ -236,7 +253,7 @@ struct StageDma {
             const int blk = (i * anw + aw) % L::A_INSTR;
             dma16(a_off[i], a + (size_t)kt * kBK, lds_addr(st + blk * 1024));
         }
-        dma4(sa_off, a_sf + (size_t)kt * (4 * BM), lds_addr(st + L::A_BYTES + L::B_BYTES + sa_blk * 256));
+        dma4(sa_off, a_sf + (size_t)kt * sa_kt, lds_addr(st + L::A_BYTES + L::B_BYTES + sa_blk * 256));
     }
     __device__ __forceinline__ void issue_b(uint8_t* st, int kt, int lane) const {
 #pragma unroll
@@ -307,7 +324,7 @@ __device__ __forceinline__ void mfma_step(v4f (&acc)[MI][NI], const Frags<MI, NI
 // l & 8 == 0, up in the others) or 4*(l & 15) + b of its 64 columns (Linear2).
 template <int BM, int MI, int NI>
 __device__ __forceinline__ void epilogue_linear1(const v4f (&acc)[MI][NI], const GemmArgs& g, int m_tile, int wrow0,
-                                                 int gcol0, const float* row_w, int lane) {
+                                                 int gcol0, const float* row_w, const int* row_tok, int lane) {
     static_assert(NI % 4 == 0, "a wave owns whole 64-column groups");
     const bool gate_lane = (lane & 8) == 0;
     const int j8 = lane & 7;
@@ -329,7 +346,7 @@ __device__ __forceinline__ void epilogue_linear1(const v4f (&acc)[MI][NI], const
             for (int ii = 0; ii < 2; ++ii) {
                 // gate lanes finish rows 0-1 of the lane's four, up lanes rows 2-3
                 const int row_local = wrow0 + mi * 16 + 4 * (lane >> 4) + (gate_lane ? ii : 2 + ii);
-                const float wgt = row_w[row_local];
+                const float wgt = row_tok[row_local] >= 0 ? row_w[row_local] : 0.0f;  // padding rows: h = 0
                 float h[4];
                 float amax = 0.0f;
 #pragma unroll
@@ -384,15 +401,16 @@ __device__ __forceinline__ void epilogue_linear2(const v4f (&acc)[MI][NI], const
 template <int BM, int MI, int NI, bool L1>
 __device__ __forceinline__ void epilogue(const v4f (&acc)[MI][NI], const GemmArgs& g, int m_tile, int wrow0,
                                          int gcol0, const float* row_w, const int* row_tok, int lane) {
-    if constexpr (L1) epilogue_linear1<BM>(acc, g, m_tile, wrow0, gcol0, row_w, lane);
+    if constexpr (L1) epilogue_linear1<BM>(acc, g, m_tile, wrow0, gcol0, row_w, row_tok, lane);
     else epilogue_linear2<BM>(acc, g, m_tile, wrow0, gcol0, row_tok, lane);
 }
 
 template <int BM, bool L1>
 __device__ __forceinline__ void load_row_tables(const GemmArgs& g, int m_tile, float* row_w, int* row_tok, int tid) {
     if (tid < BM) {
-        row_tok[tid] = g.row_token[m_tile * BM + tid];
-        if (L1) row_w[tid] = g.row_w[m_tile * BM + tid];
+        const int t = g.row_token[m_tile * BM + tid];
+        row_tok[tid] = t;
+        if (L1) row_w[tid] = t >= 0 ? g.topk_w[(size_t)t * g.topk + g.row_topk[m_tile * BM + tid]] : 0.0f;
     }
     __syncthreads();
 }
@@ -486,16 +504,21 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
 // only separate its last reads from its last MFMAs).  A group runs the
 // epilogue of a tile right after its last MFMA phase of that tile.
 //
-// Per-tile tables reach LDS through the same DMA stream, one extra
-// instruction per wave per stage so the vmcnt arithmetic stays exact:
-// group 0 loads the list entry of tile ci + 2 into desc[(ci + 2) % 3] and
-// group 1 the row tokens and top-k weights of tile ci + 1 into meta[(ci + 1)
-// % 3] (ci = the tile being multiplied; between tile changes the same load
-// repeats, rewriting identical bytes).  With KT >= 2 (NS - 1) K-steps per
-// tile every table has landed before it is read: a list entry by the time
-// its rows are fetched, the rows by the time the tile's first stage is
-// issued.  Below that the kernel runs one tile per workgroup.
-template <int BM>
+// Per-tile tables reach LDS through the same DMA stream, a fixed number of
+// extra instructions per wave per stage so the vmcnt arithmetic stays exact:
+// group 0 loads the list entry of tile ci + 2 into desc[(ci + 2) % 3];
+// group 1 loads the row tokens and top-k slots of tile ci + 1 into
+// meta[(ci + 1) % 3] (ci = the tile being multiplied; between tile changes
+// the same load repeats, rewriting identical bytes).  For Linear1 group 1
+// also gathers the top-k weights of a tile through those tables into
+// wts[.. % 3], once, with the tile's first stage (a 64-line scatter per
+// instruction, too costly to repeat every stage); its vmcnt waits count that
+// instruction where it falls.  With KT >= 2 (NS - 1) K-steps per tile
+// every table has landed before it is read: a list entry by the time its
+// rows are fetched, the rows by the time the tile's first stage is issued,
+// the weights by the time the tile's multiplication starts.  Below that the
+// kernel runs one tile per workgroup.
+template <int BM, bool L1>
 struct CfgPP {
     using L = StageLayout<BM, 512>;
     static constexpr bool SPLIT_ROWS = BM == 128;  // the groups split the rows, else the columns
@@ -506,7 +529,7 @@ struct CfgPP {
     static constexpr int SB_PW = L::SB_INSTR / 4;
     static constexpr int D0 = B_PW + SB_PW + 1;
     static constexpr int A_PW = L::A_INSTR >= 4 ? L::A_INSTR / 4 : 1;  // group 1: rows, scales, + row tables
-    static constexpr int D1 = A_PW + 1 + 1;
+    static constexpr int D1 = A_PW + 1 + 1;  // + 1 on the first stage of each tile (Linear1)
     static constexpr int MIN_KT_PERSISTENT = 2 * (L::NS - 1);
     static_assert(2 * D0 < kNoVmWait && 2 * D1 < kNoVmWait, "vmcnt range");
     static_assert(BM <= 128, "row tables hold 128 rows");
@@ -515,11 +538,12 @@ constexpr int kTableSlots = 3;
 
 template <int BM, bool L1>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
-    using C = CfgPP<BM>;
+    using C = CfgPP<BM, L1>;
     using L = typename C::L;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[L::NS * L::STAGE];
     __shared__ int desc[kTableSlots][64];   // words 0, 1: the tile's list entry {m, n << 16 | e}
-    __shared__ int meta[kTableSlots][256];  // [0, 128): row tokens; [128, 256): top-k weights (Linear1)
+    __shared__ int meta[kTableSlots][256];  // [0, 128): row tokens; [128, 256): top-k slots
+    __shared__ float wts[kTableSlots][128]; // Linear1: top-k weights of the rows
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -547,8 +571,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
         j = min(j, ntiles - 1);
         const int part = wq >> 1, half = wq & 1;
         const int row = min(half * 64 + lane, BM - 1);
-        const void* src = (L1 && part == 1) ? static_cast<const void*>(g.row_w + (size_t)m * BM)
-                                            : static_cast<const void*>(g.row_token + (size_t)m * BM);
+        const int32_t* src = (part == 1 ? g.row_topk : g.row_token) + (size_t)m * BM;
         dma4((uint32_t)row * 4, src, lds_addr(&meta[j % kTableSlots][part * 128 + half * 64]));
     };
     auto read_entry = [&](int j, TileId& t) {
@@ -597,9 +620,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
             wait_and_barrier<kNoVmWait>();                                 // B_2gs+1
             mfma_step(acc, f);
             if (++kt == KT) {
-                const int* mt = meta[ci % kTableSlots];
-                epilogue<BM, C::MI, C::NI, L1>(acc, g, ct.m, wrow0, ct.n * 512 + wcol0,
-                                               reinterpret_cast<const float*>(mt + 128), mt, lane);
+                epilogue<BM, C::MI, C::NI, L1>(acc, g, ct.m, wrow0, ct.n * 512 + wcol0, wts[ci % kTableSlots],
+                                               meta[ci % kTableSlots], lane);
                 zero(acc);
                 kt = 0;
                 ++ci;
@@ -610,19 +632,31 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
         dma.init_a(g, t0.m, meta[0], L1, wq, 4, lane);
         TileId tn;  // tile whose rows the table load fetches
         read_entry(1, tn);
+        // Linear1: byte offset into topk_w of this lane's row of the issued tile
+        const int w_row = min((wq & 1) * 64 + lane, BM - 1);
+        auto weight_offset = [&](int j) {
+            const int* mt = meta[j % kTableSlots];
+            const int t = mt[w_row];
+            return t >= 0 ? (uint32_t)(t * g.topk + mt[128 + w_row]) * 4u : 0u;
+        };
+        uint32_t w_off = L1 ? weight_offset(0) : 0u;
         auto issue = [&](int s) {
             if (s % KT == 0 && s > 0) {
                 TileId t;
                 read_entry(s / KT, t);
                 dma.init_a(g, t.m, meta[(s / KT) % kTableSlots], L1, wq, 4, lane);
+                if (L1) w_off = weight_offset(s / KT);
             }
             dma.issue_a(smem + (s % L::NS) * L::STAGE, s % KT, lane);
             load_meta(max(s - (L::NS - 1), 0) / KT + 1, tn.m);
+            if (L1 && s % KT == 0) dma4(w_off, g.topk_w, lds_addr(&wts[(s / KT) % kTableSlots][(wq & 1) * 64]));
         };
+        // does a stage in (s, s + n] start a tile (and so carry the weight gather)?
+        auto starts_tile = [&](int s, int n) { return L1 && n > 0 && ((s % KT) + n >= KT) ? 1 : 0; };
 #pragma unroll
         for (int s = 0; s < L::NS - 1; ++s)
             if (s < S) issue(s);
-        wait_stages_and_barrier<C::D1>(min(L::NS - 2, S - 1));             // B_0
+        wait_stages_and_barrier<C::D1>(min(L::NS - 2, S - 1), starts_tile(0, min(L::NS - 2, S - 1)));  // B_0
         for (int gs = 0, kt = 0, ci = 0; gs < S; ++gs) {
             wait_and_barrier<kNoVmWait>();                                 // B_2gs+1
             if (kt == 0) {
@@ -632,12 +666,14 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
             if (gs + L::NS - 1 < S) issue(gs + L::NS - 1);
             Frags<C::MI, C::NI> f;
             read_frags<BM, 512>(f, smem + (gs % L::NS) * L::STAGE, wrow0, wcol0, lane);
-            if (gs + 1 < S) wait_stages_and_barrier<C::D1>(min(L::NS - 2, S - 2 - gs));  // B_2gs+2
+            if (gs + 1 < S) {  // B_2gs+2
+                const int n = min(L::NS - 2, S - 2 - gs);
+                wait_stages_and_barrier<C::D1>(n, starts_tile(gs + 1, n));
+            }
             mfma_step(acc, f);
             if (++kt == KT) {
-                const int* mt = meta[ci % kTableSlots];
-                epilogue<BM, C::MI, C::NI, L1>(acc, g, ct.m, wrow0, ct.n * 512 + wcol0,
-                                               reinterpret_cast<const float*>(mt + 128), mt, lane);
+                epilogue<BM, C::MI, C::NI, L1>(acc, g, ct.m, wrow0, ct.n * 512 + wcol0, wts[ci % kTableSlots],
+                                               meta[ci % kTableSlots], lane);
                 zero(acc);
                 kt = 0;
                 ++ci;
@@ -664,7 +700,7 @@ hipError_t launch_bm(const GemmArgs& args, int64_t tiles, hipStream_t stream) {
     const int64_t all = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;  // one workgroup per tile
     if (gemm_bn(args.N) == 512) {
         int64_t grid = all;
-        if (args.K / kBK >= CfgPP<BM>::MIN_KT_PERSISTENT) {  // persistent: one workgroup per CU
+        if (args.K / kBK >= CfgPP<BM, L1>::MIN_KT_PERSISTENT) {  // persistent: one workgroup per CU
             const int64_t cus = cu_count() / kNumXcd * kNumXcd;
             grid = std::max<int64_t>(kNumXcd, std::min(all, cus));
         }
@@ -692,18 +728,20 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmArgs& args, hipStream_t s
 GemmArgs common_args(const GemmProblem& p) {
     GemmArgs a{};
     a.scalars = p.plan->scalars;
-    a.tiles = p.tiles;
     a.row_token = p.plan->row_token;
-    a.row_w = p.row_w;
+    a.row_topk = p.plan->row_topk;
+    a.topk = p.shape->topk;
     return a;
 }
 
 }  // namespace
 
-hipError_t launch_linear1(const GemmProblem& p, const uint8_t* x, const uint8_t* x_sf_tiled, const uint8_t* w1,
-                          const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf, hipStream_t stream) {
+hipError_t launch_linear1(const GemmProblem& p, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
+                          const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf, hipStream_t stream) {
     GemmArgs a = common_args(p);
-    a.a = x; a.a_sf = x_sf_tiled; a.b = w1; a.b_sf = w1_sf;
+    a.tiles = p.plan->tiles1;
+    a.topk_w = topk_w;
+    a.a = x; a.a_sf = x_sf; a.b = w1; a.b_sf = w1_sf;
     a.out_q = h_q; a.out_sf = h_sf; a.out_bf16 = nullptr;
     a.K = p.shape->hidden; a.N = 2 * p.shape->intermediate;
     return launch_gemm<true>(p, a, stream);
@@ -712,6 +750,7 @@ hipError_t launch_linear1(const GemmProblem& p, const uint8_t* x, const uint8_t*
 hipError_t launch_linear2(const GemmProblem& p, const uint8_t* h_q, const uint8_t* h_sf, const uint8_t* w2,
                           const uint8_t* w2_sf, uint16_t* yslot, hipStream_t stream) {
     GemmArgs a = common_args(p);
+    a.tiles = p.plan->tiles2;
     a.a = h_q; a.a_sf = h_sf; a.b = w2; a.b_sf = w2_sf;
     a.out_q = nullptr; a.out_sf = nullptr; a.out_bf16 = yslot;
     a.K = p.shape->intermediate; a.N = p.shape->hidden;

@@ -22,10 +22,15 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Routing of large inputs runs as three kernels over groups of kRouteTokensPerGroup tokens.
 constexpr int kRouteTokensPerGroup = 256;
 
+// Tile widths of the two GEMMs: 512 columns when N allows it, else 256.
+inline int gemm_bn(int n) { return n % 512 == 0 ? 512 : 256; }
+
 struct PlanLayout {
     int64_t cap = 0, max_blocks = 0, groups = 0;
+    int nt1 = 0, nt2 = 0;                  // N-tiles of Linear1 (N = 2I) and Linear2 (N = H)
+    int64_t max_tiles1 = 0, max_tiles2 = 0;
     size_t scalars = 0, counts = 0, offsets = 0, slot = 0, row_token = 0, row_topk = 0,
-           block_expert = 0, slack = 0, pull_order = 0, group_counts = 0, total = 0;
+           block_expert = 0, slack = 0, pull_order = 0, group_counts = 0, tiles1 = 0, tiles2 = 0, total = 0;
 };
 
 inline int64_t capacity_rows(const moe_shape& s) {
@@ -50,6 +55,13 @@ inline PlanLayout plan_layout(const moe_shape& s) {
     L.pull_order = take((size_t)s.num_tokens * 4);
     L.groups = (s.num_tokens + kRouteTokensPerGroup - 1) / kRouteTokensPerGroup;
     L.group_counts = take((size_t)L.groups * s.num_experts * 2 * 4);  // hit and pull counts per group
+    // GEMM tile lists: tile = (expert, M-block, N-tile), expert by expert, for each N-tile all M-blocks
+    L.nt1 = 2 * s.intermediate / gemm_bn(2 * s.intermediate);
+    L.nt2 = s.hidden / gemm_bn(s.hidden);
+    L.max_tiles1 = L.max_blocks * L.nt1;
+    L.max_tiles2 = L.max_blocks * L.nt2;
+    L.tiles1 = take((size_t)L.max_tiles1 * 8);
+    L.tiles2 = take((size_t)L.max_tiles2 * 8);
     L.total = o;
     return L;
 }
@@ -57,12 +69,8 @@ inline PlanLayout plan_layout(const moe_shape& s) {
 // Offsets (bytes) inside a forward workspace: the plan region first.
 struct ForwardLayout {
     PlanLayout plan;
-    size_t plan_base = 0, x_sf = 0, row_w = 0, tiles1 = 0, tiles2 = 0, h_q = 0, h_sf = 0, yslot = 0, total = 0;
-    int64_t max_tiles1 = 0, max_tiles2 = 0;
+    size_t plan_base = 0, h_q = 0, h_sf = 0, yslot = 0, total = 0;
 };
-
-// Tile widths of the two GEMMs: 512 columns when N allows it, else 256.
-inline int gemm_bn(int n) { return n % 512 == 0 ? 512 : 256; }
 
 inline ForwardLayout forward_layout(const moe_shape& s) {
     ForwardLayout F;
@@ -70,12 +78,6 @@ inline ForwardLayout forward_layout(const moe_shape& s) {
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, kAlign); return at; };
     F.plan_base = take(F.plan.total);
-    F.x_sf = take((size_t)F.plan.cap * (s.hidden / 32));
-    F.row_w = take((size_t)F.plan.cap * 4);
-    F.max_tiles1 = F.plan.max_blocks * (2 * s.intermediate / gemm_bn(2 * s.intermediate));
-    F.max_tiles2 = F.plan.max_blocks * (s.hidden / gemm_bn(s.hidden));
-    F.tiles1 = take((size_t)F.max_tiles1 * 8);
-    F.tiles2 = take((size_t)F.max_tiles2 * 8);
     F.h_q = take((size_t)F.plan.cap * s.intermediate);
     F.h_sf = take((size_t)F.plan.cap * (s.intermediate / 32));
     F.yslot = take((size_t)F.plan.cap * s.hidden * 2);
@@ -85,16 +87,16 @@ inline ForwardLayout forward_layout(const moe_shape& s) {
 
 struct PlanPtrs {
     int32_t *scalars, *counts, *offsets, *slot, *row_token, *row_topk, *block_expert, *slack, *pull_order,
-        *group_counts;
+        *group_counts, *tiles1, *tiles2;
+    int nt1, nt2;
 };
 
 inline PlanPtrs plan_ptrs(const PlanLayout& L, void* base) {
     char* b = static_cast<char*>(base);
-    return PlanPtrs{reinterpret_cast<int32_t*>(b + L.scalars),      reinterpret_cast<int32_t*>(b + L.counts),
-                    reinterpret_cast<int32_t*>(b + L.offsets),      reinterpret_cast<int32_t*>(b + L.slot),
-                    reinterpret_cast<int32_t*>(b + L.row_token),    reinterpret_cast<int32_t*>(b + L.row_topk),
-                    reinterpret_cast<int32_t*>(b + L.block_expert), reinterpret_cast<int32_t*>(b + L.slack),
-                    reinterpret_cast<int32_t*>(b + L.pull_order), reinterpret_cast<int32_t*>(b + L.group_counts)};
+    auto at = [&](size_t off) { return reinterpret_cast<int32_t*>(b + off); };
+    return PlanPtrs{at(L.scalars),   at(L.counts),     at(L.offsets),      at(L.slot),   at(L.row_token),
+                    at(L.row_topk),  at(L.block_expert), at(L.slack),      at(L.pull_order), at(L.group_counts),
+                    at(L.tiles1),    at(L.tiles2),     L.nt1,              L.nt2};
 }
 
 // ---- launchers (each enqueues on `stream` and returns the launch status) ----
@@ -104,21 +106,18 @@ struct GemmProblem {
     const moe_shape* shape;
     const PlanPtrs* plan;
     int64_t cap;
-    const int32_t* tiles;  // tile list of this GEMM (written by the Linear1 prep kernel)
-    const float* row_w;    // per-row top-k weights (Linear1 only)
 };
-// x_sf_tiled / h_sf: activation scales in the per-row-block layout [cap/BM][K/128][BM][4];
-// w*, w*_sf: weights in the tiled layout of moe_prepare.hip.
-hipError_t launch_linear1(const GemmProblem& g, const uint8_t* x, const uint8_t* x_sf_tiled,
+// Linear1 gathers its A rows and their scales (x [T, H], x_sf [T, H/32]) and
+// the top-k weights through the plan's row tables; Linear2 reads h_q and h_sf
+// (per-row-block layout [cap/BM][I/128][BM][4]) as the Linear1 epilogue wrote
+// them.  w*, w*_sf: weights in the tiled layout of moe_prepare.hip.
+hipError_t launch_linear1(const GemmProblem& g, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
                           const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf,
                           hipStream_t stream);
 hipError_t launch_linear2(const GemmProblem& g, const uint8_t* h_q, const uint8_t* h_sf, const uint8_t* w2,
                           const uint8_t* w2_sf, uint16_t* yslot, hipStream_t stream);
 hipError_t launch_tile_weights(int which, int N, int K, int E, const uint8_t* w, const uint8_t* w_sf,
                                uint8_t* w_out, uint8_t* sf_out, hipStream_t stream);
-hipError_t launch_prep_linear1(const moe_shape& s, const uint8_t* x_sf, const float* topk_w, const PlanPtrs& p,
-                               int64_t cap, int nt1, int nt2, uint32_t* xsf_out, float* row_w, int32_t* tiles1,
-                               int32_t* tiles2, hipStream_t stream);
 hipError_t launch_combine(const moe_shape& s, const uint16_t* yslot, const int32_t* slot, uint16_t* y,
                           hipStream_t stream);
 

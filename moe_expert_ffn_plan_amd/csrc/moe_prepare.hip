@@ -25,10 +25,9 @@
 //   Linear2 (N = H): column 64G + 4j + b, so a lane owns four adjacent BF16
 //     outputs (8 bytes).
 //
-// The activation-side scales get the analogous per-row-block layout
-//   [R/BM][K/128][BM rows][4 B]
-// (prep_linear1_kernel builds it for Linear1's gathered rows; the Linear1
-// epilogue writes Linear2's that way directly).
+// Linear2's activation scales use the analogous per-row-block layout
+//   [R/BM][K/128][BM rows][4 B],
+// written that way by the Linear1 epilogue.
 #include "moe_internal.h"
 
 namespace moe {
@@ -82,58 +81,6 @@ __global__ __launch_bounds__(kThreads) void tile_weight_scale_kernel(const uint8
     out[s] = *reinterpret_cast<const uint32_t*>(sf + (e * N + col) * (K / 32) + (int64_t)kt * 4);
 }
 
-// Per-forward preparation for Linear1 (one pass over the padded rows and the tiles):
-//  * x_sf_tiled[(blk * KT + kt) * BM + r] = x_sf[row_token[blk * BM + r]][kt*4 .. kt*4+3]
-//    (padding rows read token 0: their top-k weight is 0, so they produce h = 0);
-//  * row_w[r] = topk_w[row_token[r], row_topk[r]] (0 for padding rows);
-//  * the tile lists of both GEMMs: tile L = (expert e, M-tile m, N-tile n), listed expert by
-//    expert, for each N-tile all M-tiles of the expert; stored as two ints {m, n << 16 | e}.
-__global__ __launch_bounds__(kThreads) void prep_linear1_kernel(const uint8_t* __restrict__ x_sf,
-                                                                const float* __restrict__ topk_w, int topk,
-                                                                const int32_t* __restrict__ scalars,
-                                                                const int32_t* __restrict__ offsets,
-                                                                const int32_t* __restrict__ row_token,
-                                                                const int32_t* __restrict__ row_topk, int E, int K,
-                                                                int bm, int nt1, int nt2, uint32_t* __restrict__ xsf_out,
-                                                                float* __restrict__ row_w, int32_t* __restrict__ tiles1,
-                                                                int32_t* __restrict__ tiles2) {
-    const int KT = K / 128;
-    const int r_pad = scalars[0];
-    const int mt = r_pad / bm;
-    const int64_t n_sf = (int64_t)r_pad * KT;
-    const int64_t n1 = (int64_t)mt * nt1, n2 = (int64_t)mt * nt2;
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    for (int64_t s = t0; s < n_sf; s += stride) {
-        const int r = (int)(s % bm);
-        int64_t t = s / bm;
-        const int kt = (int)(t % KT);
-        const int blk = (int)(t / KT);
-        const int tok = row_token[blk * bm + r];
-        xsf_out[s] = *reinterpret_cast<const uint32_t*>(x_sf + (int64_t)(tok >= 0 ? tok : 0) * (K / 32) + kt * 4);
-    }
-    for (int64_t r = t0; r < r_pad; r += stride) {
-        const int tok = row_token[r];
-        row_w[r] = tok >= 0 ? topk_w[(int64_t)tok * topk + row_topk[r]] : 0.0f;
-    }
-    for (int64_t L = t0; L < n1 + n2; L += stride) {
-        const bool first = L < n1;
-        const int nt = first ? nt1 : nt2;
-        const int l = (int)(first ? L : L - n1);
-        int lo = 0, hi = E - 1;  // largest e whose first tile is <= l
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if ((offsets[mid] / bm) * nt <= l) lo = mid; else hi = mid - 1;
-        }
-        const int mb0 = offsets[lo] / bm;
-        const int me = offsets[lo + 1] / bm - mb0;
-        const int local = l - mb0 * nt;
-        int32_t* out = (first ? tiles1 : tiles2) + 2 * (int64_t)l;
-        out[0] = mb0 + local % me;
-        out[1] = ((local / me) << 16) | lo;
-    }
-}
-
 }  // namespace
 
 hipError_t launch_tile_weights(int which, int N, int K, int E, const uint8_t* w, const uint8_t* w_sf,
@@ -147,17 +94,6 @@ hipError_t launch_tile_weights(int which, int N, int K, int E, const uint8_t* w,
         hipLaunchKernelGGL(tile_weight_scale_kernel, dim3((unsigned)((words + kThreads - 1) / kThreads)),
                            dim3(kThreads), 0, stream, w_sf, which, N, K, words,
                            reinterpret_cast<uint32_t*>(sf_out));
-    return hipGetLastError();
-}
-
-hipError_t launch_prep_linear1(const moe_shape& s, const uint8_t* x_sf, const float* topk_w, const PlanPtrs& p,
-                               int64_t cap, int nt1, int nt2, uint32_t* xsf_out, float* row_w, int32_t* tiles1,
-                               int32_t* tiles2, hipStream_t stream) {
-    const int64_t n = cap * (s.hidden / 128);
-    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n + kThreads - 1) / kThreads, 1024));
-    hipLaunchKernelGGL(prep_linear1_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, x_sf, topk_w, s.topk,
-                       p.scalars, p.offsets, p.row_token, p.row_topk, s.num_experts, s.hidden, s.block_m, nt1, nt2,
-                       xsf_out, row_w, tiles1, tiles2);
     return hipGetLastError();
 }
 

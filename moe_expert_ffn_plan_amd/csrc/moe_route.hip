@@ -76,6 +76,25 @@ __device__ __forceinline__ int local_expert(const int64_t* ids, int64_t h, int64
     return (le >= 0 && le < E) ? (int)le : -1;
 }
 
+// GEMM tile lists from the padded offsets (LDS): for a GEMM with nt N-tiles,
+// expert e's tiles start at (soff[e] / bm) * nt and run N-tile by N-tile over
+// all of e's M-blocks; entry l = {m, n << 16 | e}.
+__device__ void write_tiles(const int32_t* soff, int E, int bm, int nt, int32_t* __restrict__ tiles) {
+    const int total = soff[E] / bm * nt;
+    for (int l = threadIdx.x; l < total; l += blockDim.x) {
+        int lo = 0, hi = E - 1;  // largest e whose first tile is <= l (that expert has rows)
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (soff[mid] / bm * nt <= l) lo = mid; else hi = mid - 1;
+        }
+        const int mb0 = soff[lo] / bm;
+        const int me = soff[lo + 1] / bm - mb0;
+        const int local = l - mb0 * nt;
+        tiles[2 * l] = mb0 + local % me;
+        tiles[2 * l + 1] = ((local / me) << 16) | lo;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restrict__ ids, int T, int k, int E,
                                                          int expert_begin, int bm, PlanPtrs p) {
     extern __shared__ int32_t lds[];
@@ -187,6 +206,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
             p.row_topk[q] = -1;
         }
     }
+    write_tiles(soff, E, bm, p.nt1, p.tiles1);
+    write_tiles(soff, E, bm, p.nt2, p.tiles2);
     __syncthreads();
 
     // ---- pass 5: pull order = tokens with a hit, by smallest local expert, then t
@@ -317,6 +338,7 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(int E, int bm, int
     int32_t* chunk = scratch + 64;  // [kScanChunkWords]
     const int tid = threadIdx.x;
     const int gpc = max(1, kScanChunkWords / (2 * E));  // groups per chunk
+    const bool one_chunk = groups <= gpc;               // then the group prefixes stay in LDS
     int run = 0, prun = 0;                              // running sums of expert `tid`
     for (int g0 = 0; g0 < groups; g0 += gpc) {
         const int ng = min(gpc, groups - g0);
@@ -334,11 +356,13 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(int E, int bm, int
                 prun += cq;
             }
         __syncthreads();
-        for (int i = tid; i < ng * E; i += kThreads) {
-            gcounts[(size_t)g0 * E + i] = chunk[i];
-            gcounts[((size_t)groups + g0) * E + i] = chunk[ng * E + i];
+        if (!one_chunk) {
+            for (int i = tid; i < ng * E; i += kThreads) {
+                gcounts[(size_t)g0 * E + i] = chunk[i];
+                gcounts[((size_t)groups + g0) * E + i] = chunk[ng * E + i];
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
     if (tid < E) {
         scnt[tid] = run;
@@ -367,10 +391,18 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(int E, int bm, int
         p.scalars[3] = incl_pad / bm;   // n_blocks
     }
     __syncthreads();
-    for (int64_t i = tid; i < (int64_t)groups * E; i += kThreads) {
-        const int e = (int)(i % E);
-        gcounts[i] += soff[e];
-        gcounts[(size_t)groups * E + i] += pbase[e];
+    if (one_chunk) {
+        for (int i = tid; i < groups * E; i += kThreads) {
+            const int e = i % E;
+            gcounts[i] = chunk[i] + soff[e];
+            gcounts[(size_t)groups * E + i] = chunk[groups * E + i] + pbase[e];
+        }
+    } else {
+        for (int64_t i = tid; i < (int64_t)groups * E; i += kThreads) {
+            const int e = (int)(i % E);
+            gcounts[i] += soff[e];
+            gcounts[(size_t)groups * E + i] += pbase[e];
+        }
     }
     const int n_blocks = soff[E] / bm;
     for (int b = tid; b < n_blocks; b += kThreads) {
@@ -388,6 +420,8 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(int E, int bm, int
             p.row_topk[q] = -1;
         }
     }
+    write_tiles(soff, E, bm, p.nt1, p.tiles1);
+    write_tiles(soff, E, bm, p.nt2, p.tiles2);
 }
 
 __global__ __launch_bounds__(kGThreads) void route_scatter_kernel(const int64_t* __restrict__ ids, int T, int k, int E,
