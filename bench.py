@@ -22,6 +22,7 @@ oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +34,24 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer useful TFLOP/s + tokens/s at 1 GPU; % of scaled-MFMA peak / HBM BW"
 PEAK_MFMA_TFLOPS = 5000.0      # MI355X dense FP8 MFMA; FP8 x FP4 scaled MFMA issues at this rate
 PEAK_HBM_GBS = 8000.0
+
+
+def linear1_traffic(workload: str):
+    """HBM bytes per Linear1 launch from the committed rocprofv3 byte-counter summary, when it was taken on
+    this workload with the current GEMM source (its sha256 is recorded there); else None."""
+    path = os.path.join(ROOT, "profiles", f"linear1_gemm_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            key, val = line[2:].split(":", 1)
+            fields[key.strip()] = val.strip()
+    src = os.path.join(ROOT, "moe_expert_ffn_plan_amd", "csrc", "moe_gemm.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("kernel_source_sha256") != digest or fields.get("workload") != workload:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(w, d_gpu, sample_tokens: int, min_seconds: float = 10.0):
@@ -164,7 +183,7 @@ def main() -> int:
     kname = ("gemm_pp_kernel<%d, true>" if (2 * I) % 512 == 0 else "gemm4_kernel<%d, true>") % w.block_m
     roofline = {"kernel": f"Linear1 grouped GEMM ({kname})", "bound": "mfma", "achieved": round(l1_tflops, 2),
                 "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(l1_tflops / PEAK_MFMA_TFLOPS, 4),
-                "traffic": None}
+                "traffic": linear1_traffic(w.name)}
     out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "fp8e4m3 x fp4e2m1 (fp32 accumulate)", "data": "synthetic",
