@@ -279,7 +279,8 @@ struct Frags {
     int sa[MI], sb[NI];
 };
 
-template <int BM, int BN, int MI, int NI>
+// B fragments of all NI blocks and A fragments of blocks [MI0, MI1) of one K-step.
+template <int BM, int BN, int MI, int NI, int MI0 = 0, int MI1 = MI, bool WITH_B = true>
 __device__ __forceinline__ void read_frags(Frags<MI, NI>& f, const uint8_t* st, int wrow0, int wcol0, int lane) {
     using L = StageLayout<BM, BN>;
     const int gq = lane >> 4;
@@ -287,14 +288,16 @@ __device__ __forceinline__ void read_frags(Frags<MI, NI>& f, const uint8_t* st, 
     const uint8_t* Bt = st + L::A_BYTES;
     const uint32_t* SA = reinterpret_cast<const uint32_t*>(st + L::A_BYTES + L::B_BYTES);
     const uint32_t* SB = SA + L::SA_WORDS;
+    if constexpr (WITH_B) {
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-        const int col = wcol0 + ni * 16 + (lane & 15);
-        f.b[ni] = *reinterpret_cast<const v4i*>(Bt + col * (kBK / 2) + ((gq ^ ((col >> 1) & 3)) << 4));
-        f.sb[ni] = (int)(SB[col] >> (8 * gq));
+        for (int ni = 0; ni < NI; ++ni) {
+            const int col = wcol0 + ni * 16 + (lane & 15);
+            f.b[ni] = *reinterpret_cast<const v4i*>(Bt + col * (kBK / 2) + ((gq ^ ((col >> 1) & 3)) << 4));
+            f.sb[ni] = (int)(SB[col] >> (8 * gq));
+        }
     }
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
+    for (int mi = MI0; mi < MI1; ++mi) {
         const int row = wrow0 + mi * 16 + (lane & 15);
         const int sw = (row >> 1) & 7;
         const v4i lo = *reinterpret_cast<const v4i*>(A + row * kBK + ((gq ^ sw) << 4));
@@ -304,10 +307,11 @@ __device__ __forceinline__ void read_frags(Frags<MI, NI>& f, const uint8_t* st, 
     }
 }
 
-template <int MI, int NI>
+// MFMAs of A blocks [MI0, MI1) against all B blocks.
+template <int MI, int NI, int MI0 = 0, int MI1 = MI>
 __device__ __forceinline__ void mfma_step(v4f (&acc)[MI][NI], const Frags<MI, NI>& f) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = MI0; mi < MI1; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
             const v8i b = v8i{f.b[ni][0], f.b[ni][1], f.b[ni][2], f.b[ni][3], 0, 0, 0, 0};
@@ -615,10 +619,17 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
             wait_stages_and_barrier<C::D0>(min(L::NS - 2, S - 1 - gs));  // B_2gs
             if (kt == 0) read_entry(ci, ct);
             if (gs + L::NS - 1 < S) issue(gs + L::NS - 1);
+            // this group's read phase carries its DMA issue as well, so it reads only the first half
+            // of its A fragments here and the second half at the start of its MFMA phase (stage gs is
+            // still intact then: it is refilled only after B_2gs+2)
+            constexpr int MH = C::MI / 2;
+            const uint8_t* st = smem + (gs % L::NS) * L::STAGE;
             Frags<C::MI, C::NI> f;
-            read_frags<BM, 512>(f, smem + (gs % L::NS) * L::STAGE, wrow0, wcol0, lane);
+            read_frags<BM, 512, C::MI, C::NI, 0, MH>(f, st, wrow0, wcol0, lane);
             wait_and_barrier<kNoVmWait>();                                 // B_2gs+1
-            mfma_step(acc, f);
+            read_frags<BM, 512, C::MI, C::NI, MH, C::MI, false>(f, st, wrow0, wcol0, lane);
+            mfma_step<C::MI, C::NI, 0, MH>(acc, f);
+            mfma_step<C::MI, C::NI, MH, C::MI>(acc, f);
             if (++kt == KT) {
                 epilogue<BM, C::MI, C::NI, L1>(acc, g, ct.m, wrow0, ct.n * 512 + wcol0, wts[ci % kTableSlots],
                                                meta[ci % kTableSlots], lane);
