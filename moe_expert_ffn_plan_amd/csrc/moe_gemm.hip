@@ -84,9 +84,13 @@ struct GemmArgs {
     int K, N, topk;
 };
 
-__device__ __forceinline__ float bf16_round(float v) { return (float)(__bf16)v; }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+// Two floats to BF16 (round to nearest even) with one v_cvt_pk_bf16_f32: lo in bits 0-15.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
 
 // UE8M0 code of the smallest power of two 2^s with amax / 2^s <= 448, from
 // the exponent and mantissa bits (448 = 1.75 * 2^8).
@@ -307,17 +311,23 @@ __device__ __forceinline__ void read_frags(Frags<MI, NI>& f, const uint8_t* st, 
     }
 }
 
-// MFMAs of A blocks [MI0, MI1) against all B blocks.
-template <int MI, int NI, int MI0 = 0, int MI1 = MI>
-__device__ __forceinline__ void mfma_step(v4f (&acc)[MI][NI], const Frags<MI, NI>& f) {
+// MFMAs of A blocks [MI0, MI1) against all B blocks; FIRST starts the accumulators from zero
+// (the instruction's C operand is the inline constant 0, so no register clearing is needed).
+template <int MI, int NI, int MI0 = 0, int MI1 = MI, bool FIRST = false>
+__device__ __forceinline__ void mfma_blocks(v4f (&acc)[MI][NI], const Frags<MI, NI>& f) {
 #pragma unroll
     for (int mi = MI0; mi < MI1; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
             const v8i b = v8i{f.b[ni][0], f.b[ni][1], f.b[ni][2], f.b[ni][3], 0, 0, 0, 0};
-            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.a[mi], b, acc[mi][ni], 0, 4, 0,
-                                                                            f.sa[mi], 0, f.sb[ni]);
+            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                f.a[mi], b, FIRST ? v4f{0.f, 0.f, 0.f, 0.f} : acc[mi][ni], 0, 4, 0, f.sa[mi], 0, f.sb[ni]);
         }
+}
+template <int MI, int NI, int MI0 = 0, int MI1 = MI>
+__device__ __forceinline__ void mfma_step(v4f (&acc)[MI][NI], const Frags<MI, NI>& f, bool first) {
+    if (first) mfma_blocks<MI, NI, MI0, MI1, true>(acc, f);
+    else mfma_blocks<MI, NI, MI0, MI1, false>(acc, f);
 }
 
 // ---- epilogues: straight from the accumulators to global memory.
@@ -355,8 +365,11 @@ __device__ __forceinline__ void epilogue_linear1(const v4f (&acc)[MI][NI], const
                 float amax = 0.0f;
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    const float gv = bf16_round(gate_lane ? acc[mi][grp * 4 + b][ii] : other[b][2 + ii]);
-                    const float uv = bf16_round(gate_lane ? other[b][ii] : acc[mi][grp * 4 + b][2 + ii]);
+                    // gate and up rounded to BF16 together, then widened back to FP32
+                    const uint32_t gu = pack_bf16(gate_lane ? acc[mi][grp * 4 + b][ii] : other[b][2 + ii],
+                                                  gate_lane ? other[b][ii] : acc[mi][grp * 4 + b][2 + ii]);
+                    const float gv = __uint_as_float(gu << 16);
+                    const float uv = __uint_as_float(gu & 0xFFFF0000u);
                     // silu(g) = g / (1 + 2^(-g log2 e)) with the hardware exp2 and reciprocal
                     const float s = gv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv * kLog2e));
                     h[b] = (s * uv) * wgt;
@@ -395,8 +408,8 @@ __device__ __forceinline__ void epilogue_linear2(const v4f (&acc)[MI][NI], const
             uint8_t* out = reinterpret_cast<uint8_t*>(g.out_bf16);
 #pragma unroll
             for (int grp = 0; grp < NI / 4; ++grp) {
-                const uint32_t lo = bf16_bits(acc[mi][grp * 4 + 0][i]) | (bf16_bits(acc[mi][grp * 4 + 1][i]) << 16);
-                const uint32_t hi = bf16_bits(acc[mi][grp * 4 + 2][i]) | (bf16_bits(acc[mi][grp * 4 + 3][i]) << 16);
+                const uint32_t lo = pack_bf16(acc[mi][grp * 4 + 0][i], acc[mi][grp * 4 + 1][i]);
+                const uint32_t hi = pack_bf16(acc[mi][grp * 4 + 2][i], acc[mi][grp * 4 + 3][i]);
                 *reinterpret_cast<uint2*>(out + (off + (uint32_t)(grp * 128))) = uint2{lo, hi};
             }
         }
@@ -417,14 +430,6 @@ __device__ __forceinline__ void load_row_tables(const GemmArgs& g, int m_tile, f
         if (L1) row_w[tid] = t >= 0 ? g.topk_w[(size_t)t * g.topk + g.row_topk[m_tile * BM + tid]] : 0.0f;
     }
     __syncthreads();
-}
-
-template <int MI, int NI>
-__device__ __forceinline__ void zero(v4f (&acc)[MI][NI]) {
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = v4f{0.f, 0.f, 0.f, 0.f};
 }
 
 // ============================================================================
@@ -471,7 +476,6 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
 
     const int wrow0 = (w / C::WN) * C::WTM, wcol0 = (w % C::WN) * C::WTN;
     v4f acc[C::MI][C::NI];
-    zero(acc);
 #pragma unroll
     for (int s = 0; s < L::NS - 1; ++s)
         if (s < KT) issue(s);
@@ -480,7 +484,7 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
         if (kt + L::NS - 1 < KT) issue(kt + L::NS - 1);
         Frags<C::MI, C::NI> f;
         read_frags<BM, 256>(f, smem + (kt % L::NS) * L::STAGE, wrow0, wcol0, lane);
-        mfma_step(acc, f);
+        mfma_step(acc, f, kt == 0);
     }
     epilogue<BM, C::MI, C::NI, L1>(acc, g, t.m, wrow0, t.n * 256 + wcol0, row_w, row_tok, lane);
 }
@@ -587,9 +591,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
 
     const int wrow0 = C::SPLIT_ROWS ? grp * C::WTM : 0;
     const int wcol0 = C::SPLIT_ROWS ? wq * C::WTN : grp * 256 + wq * C::WTN;
-    v4f acc[C::MI][C::NI];
-    zero(acc);
-    TileId ct;  // tile being multiplied
+    v4f acc[C::MI][C::NI];  // set by the first K-step of every tile
+    TileId ct;              // tile being multiplied
 
     // ---- prologue: list entries of tiles 0 and 1, then the rows of tile 0
     if (grp == 0) load_desc(wq & 1);
@@ -628,12 +631,11 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
             read_frags<BM, 512, C::MI, C::NI, 0, MH>(f, st, wrow0, wcol0, lane);
             wait_and_barrier<kNoVmWait>();                                 // B_2gs+1
             read_frags<BM, 512, C::MI, C::NI, MH, C::MI, false>(f, st, wrow0, wcol0, lane);
-            mfma_step<C::MI, C::NI, 0, MH>(acc, f);
-            mfma_step<C::MI, C::NI, MH, C::MI>(acc, f);
+            mfma_step<C::MI, C::NI, 0, MH>(acc, f, kt == 0);
+            mfma_step<C::MI, C::NI, MH, C::MI>(acc, f, kt == 0);
             if (++kt == KT) {
                 epilogue<BM, C::MI, C::NI, L1>(acc, g, ct.m, wrow0, ct.n * 512 + wcol0, wts[ci % kTableSlots],
                                                meta[ci % kTableSlots], lane);
-                zero(acc);
                 kt = 0;
                 ++ci;
             }
@@ -681,11 +683,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
                 const int n = min(L::NS - 2, S - 2 - gs);
                 wait_stages_and_barrier<C::D1>(n, starts_tile(gs + 1, n));
             }
-            mfma_step(acc, f);
+            mfma_step(acc, f, kt == 0);
             if (++kt == KT) {
                 epilogue<BM, C::MI, C::NI, L1>(acc, g, ct.m, wrow0, ct.n * 512 + wcol0, wts[ci % kTableSlots],
                                                meta[ci % kTableSlots], lane);
-                zero(acc);
                 kt = 0;
                 ++ci;
             }
