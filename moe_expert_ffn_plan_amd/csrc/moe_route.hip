@@ -8,8 +8,10 @@
 // expert follow ascending flat hit order t*k + j, so the tables are
 // deterministic (the pages' kernels take slots with atomics instead).
 //
-// Design: one 1024-thread workgroup (16 waves).  Each wave owns a contiguous
-// range of hits.  Pass 1 counts hits per (wave, expert) with LDS atomics;
+// Design: one 1024-thread workgroup (16 waves) for up to 32768 hits.  The
+// local expert id of every hit is first staged in LDS as int16; every later
+// pass reads it from there.  Each wave owns a contiguous range of hits.  Pass
+// 1 counts hits per (wave, expert) with LDS atomics;
 // pass 2 turns those into per-wave bases with a scan over waves and a
 // block-wide scan over experts; pass 3 re-walks each wave's hits in order,
 // 64 at a time, and ranks equal experts inside the batch with a ballot
@@ -33,7 +35,6 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kUnroll = 4;  // 64-hit batches a lane keeps in flight
 
 __device__ __forceinline__ uint64_t lanes_lt() { return (1ull << (threadIdx.x & 63)) - 1ull; }
 
@@ -71,10 +72,6 @@ __device__ int block_inclusive_scan(int v, int* scratch) {
     return v;
 }
 
-__device__ __forceinline__ int local_expert(const int64_t* ids, int64_t h, int64_t begin, int E) {
-    const int64_t le = ids[h] - begin;
-    return (le >= 0 && le < E) ? (int)le : -1;
-}
 
 // GEMM tile lists from the padded offsets (LDS): for a GEMM with nt N-tiles,
 // expert e's tiles start at (soff[e] / bm) * nt and run N-tile by N-tile over
@@ -95,36 +92,49 @@ __device__ void write_tiles(const int32_t* soff, int E, int bm, int nt, int32_t*
     }
 }
 
+// Largest input the one-workgroup kernel can hold (its local expert ids sit in LDS as int16), and the
+// size up to which it is used: beyond a few thousand hits its scattered table stores from a single CU
+// cost more than the extra launch of the multi-workgroup path.
+constexpr int kSingleMaxHits = 32768;
+constexpr int kSingleWorkgroupHits = 4096;
+
 __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restrict__ ids, int T, int k, int E,
                                                          int expert_begin, int bm, PlanPtrs p) {
-    extern __shared__ int32_t lds[];
-    int32_t* wcnt = lds;                 // [kWaves][E] per-wave counters, later per-wave bases
-    int32_t* soff = wcnt + kWaves * E;   // [E+1] padded offsets
-    int32_t* scnt = soff + E + 1;        // [E] counts
-    int32_t* sbase = scnt + E;           // [E+1] pull-order bases
-    int32_t* scratch = sbase + E + 1;    // [64]
+    __shared__ int16_t le[kSingleMaxHits];        // local expert of every hit, -1 if not local
+    __shared__ int32_t wcnt[kWaves * kMaxExperts]; // per-wave counters, later per-wave bases
+    __shared__ int32_t soff[kMaxExperts + 1];      // padded offsets
+    __shared__ int32_t scnt[kMaxExperts];          // counts (later pull counts)
+    __shared__ int32_t sbase[kMaxExperts + 1];     // pull-order bases
+    __shared__ int32_t scratch[64];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     const int64_t begin = expert_begin;
+    const int nh = T * k;
 
+    // ---- pass 0: ids -> local experts in LDS (8 loads in flight per thread), counters cleared
+    for (int base = 0; base < nh; base += 8 * kThreads) {
+        int64_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int h = base + u * kThreads + tid;
+            v[u] = h < nh ? ids[h] - begin : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int h = base + u * kThreads + tid;
+            if (h < nh) le[h] = (int16_t)((v[u] >= 0 && v[u] < E) ? v[u] : -1);
+        }
+    }
     for (int i = tid; i < kWaves * E; i += kThreads) wcnt[i] = 0;
     __syncthreads();
 
-    // ---- pass 1: hits per (wave, expert)
-    const int64_t nh = (int64_t)T * k;
-    const int64_t per_wave = (nh + kWaves * 64 - 1) / (kWaves * 64) * 64;
-    const int64_t h0 = (int64_t)w * per_wave;
-    const int64_t h1 = min(nh, h0 + per_wave);
-    for (int64_t base = h0; base < h1; base += 64 * kUnroll) {
-        int e[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t h = base + u * 64 + lane;
-            e[u] = h < h1 ? local_expert(ids, h, begin, E) : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            if (e[u] >= 0) atomicAdd(&wcnt[w * E + e[u]], 1);
+    // ---- pass 1: hits per (wave, expert); wave w owns the contiguous hits [h0, h1)
+    const int per_wave = (nh + kWaves * 64 - 1) / (kWaves * 64) * 64;
+    const int h0 = min(nh, w * per_wave);
+    const int h1 = min(nh, h0 + per_wave);
+    for (int h = h0 + lane; h < h1; h += 64) {
+        const int e = le[h];
+        if (e >= 0) atomicAdd(&wcnt[w * E + e], 1);
     }
     __syncthreads();
 
@@ -159,34 +169,26 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
     }
     __syncthreads();
 
-    // ---- pass 3: stable scatter of hits into rows
-    for (int64_t base = h0; base < h1; base += 64 * kUnroll) {
-        int e[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t h = base + u * 64 + lane;
-            e[u] = h < h1 ? local_expert(ids, h, begin, E) : -1;
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t h = base + u * 64 + lane;
-            const bool valid = e[u] >= 0;
-            const uint64_t peers = match_peers(valid, e[u], nbits);
-            if (valid) {
-                const int rank = __popcll(peers & lanes_lt());
-                const int cur = wcnt[w * E + e[u]];
-                const int row = soff[e[u]] + cur + rank;
-                p.slot[h] = row;
-                p.row_token[row] = (int)(h / k);
-                p.row_topk[row] = (int)(h % k);
-                if (rank == 0) wcnt[w * E + e[u]] = cur + __popcll(peers);
-            } else if (h < h1) {
-                p.slot[h] = -1;
-            }
+    // ---- pass 3: stable scatter of hits into rows, 64 at a time in flat order
+    for (int base = h0; base < h1; base += 64) {
+        const int h = base + lane;
+        const int e = h < h1 ? le[h] : -1;
+        const bool valid = e >= 0;
+        const uint64_t peers = match_peers(valid, e, nbits);
+        if (valid) {
+            const int rank = __popcll(peers & lanes_lt());
+            const int cur = wcnt[w * E + e];
+            const int row = soff[e] + cur + rank;
+            p.slot[h] = row;
+            p.row_token[row] = h / k;
+            p.row_topk[row] = h % k;
+            if (rank == 0) wcnt[w * E + e] = cur + __popcll(peers);
+        } else if (h < h1) {
+            p.slot[h] = -1;
         }
     }
 
-    // ---- pass 4: per-block expert and slack; padding rows marked -1
+    // ---- pass 4: per-block expert and slack; padding rows marked -1; GEMM tile lists
     const int r_pad = soff[E];
     const int n_blocks = r_pad / bm;
     for (int b = tid; b < n_blocks; b += kThreads) {
@@ -214,15 +216,18 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
     for (int i = tid; i < kWaves * E; i += kThreads) wcnt[i] = 0;
     __syncthreads();
     const int tper = (T + kWaves * 64 - 1) / (kWaves * 64) * 64;
-    const int t0 = w * tper, t1 = min(T, t0 + tper);
+    const int t0 = min(T, w * tper), t1 = min(T, t0 + tper);
+    auto smallest = [&](int t) {
+        int emin = E;
+        for (int j = 0; j < k; ++j) {
+            const int e = le[t * k + j];
+            if (e >= 0 && e < emin) emin = e;
+        }
+        return emin;
+    };
     for (int base = t0; base < t1; base += 64) {
         const int t = base + lane;
-        int emin = E;
-        if (t < t1)
-            for (int j = 0; j < k; ++j) {
-                const int e = local_expert(ids, (int64_t)t * k + j, begin, E);
-                if (e >= 0 && e < emin) emin = e;
-            }
+        const int emin = t < t1 ? smallest(t) : E;
         if (emin < E) atomicAdd(&wcnt[w * E + emin], 1);
     }
     __syncthreads();
@@ -244,12 +249,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
     __syncthreads();
     for (int base = t0; base < t1; base += 64) {
         const int t = base + lane;
-        int emin = E;
-        if (t < t1)
-            for (int j = 0; j < k; ++j) {
-                const int e = local_expert(ids, (int64_t)t * k + j, begin, E);
-                if (e >= 0 && e < emin) emin = e;
-            }
+        const int emin = t < t1 ? smallest(t) : E;
         const bool valid = emin < E;
         const uint64_t peers = match_peers(valid, emin, nbits);
         if (valid) {
@@ -487,14 +487,167 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_kernel(const int64_t*
     }
 }
 
+// Count-then-scatter path without a separate scan: every scatter workgroup reads the whole table of
+// per-group counts (groups x E hit counts and pull counts, small for the inputs it is used for) and
+// computes the scan itself, so all of them agree on the offsets; workgroup g then scatters its own
+// group, and the workgroups share the block tables, padding rows and tile lists by striding.
+constexpr int kFusedScanMaxWords = 65536;  // groups * E up to this takes the two-kernel path
+
+__global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int64_t* __restrict__ ids, int T, int k,
+                                                                      int E, int expert_begin, int groups, int bm,
+                                                                      const int32_t* __restrict__ gcounts,
+                                                                      PlanPtrs p) {
+    extern __shared__ int32_t lds[];
+    int32_t* wh = lds;                      // [kGWaves][E] running hit rows
+    int32_t* wp = wh + kGWaves * E;         // [kGWaves][E] running pull positions
+    int32_t* soff = wp + kGWaves * E;       // [E+1] padded offsets
+    int32_t* scnt = soff + E + 1;           // [E] hit counts (all groups)
+    int32_t* pbase = scnt + E;              // [E+1] pull bases
+    int32_t* gh = pbase + E + 1;            // [E] this group's first row of each expert (before soff)
+    int32_t* gp = gh + E;                   // [E] this group's first pull position (before pbase)
+    int32_t* scratch = gp + E;              // [64]
+    int16_t* le = reinterpret_cast<int16_t*>(scratch + 64);  // [256 * k]
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = blockIdx.x;
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    for (int i = tid; i < 2 * kGWaves * E; i += kGThreads) lds[i] = 0;
+    const int tg0 = g * kRouteTokensPerGroup, tg1 = min(T, tg0 + kRouteTokensPerGroup);
+    load_group_experts(ids, (int64_t)tg0 * k, (int64_t)tg1 * k, k, expert_begin, E, le);
+
+    // ---- scan of the group counts: totals and this group's bases per expert
+    for (int e = tid; e < E; e += kGThreads) {
+        int run = 0, prun = 0, mine = 0, pmine = 0;
+        for (int gg = 0; gg < groups; ++gg) {
+            if (gg == g) { mine = run; pmine = prun; }
+            run += gcounts[(size_t)gg * E + e];
+            prun += gcounts[((size_t)groups + gg) * E + e];
+        }
+        scnt[e] = run;
+        gh[e] = mine;
+        gp[e] = pmine;
+        pbase[e + 1] = prun;  // pull totals for now
+    }
+    __syncthreads();
+    // exclusive scans over experts (E <= 512 = 2 * kGThreads): thread t owns experts 2t and 2t+1
+    {
+        int padded, pulls, cnt;
+        const int e0 = 2 * tid, e1 = 2 * tid + 1;
+        const int c0 = e0 < E ? scnt[e0] : 0, c1 = e1 < E ? scnt[e1] : 0;
+        const int p0 = e0 < E ? pbase[e0 + 1] : 0, p1 = e1 < E ? pbase[e1 + 1] : 0;
+        const int pad0 = (c0 + bm - 1) / bm * bm, pad1 = (c1 + bm - 1) / bm * bm;
+        padded = pad0 + pad1;
+        pulls = p0 + p1;
+        cnt = c0 + c1;
+        const int incl_pad = block_inclusive_scan(padded, scratch);
+        const int incl_pull = block_inclusive_scan(pulls, scratch);
+        const int incl_cnt = block_inclusive_scan(cnt, scratch);
+        if (e0 < E) { soff[e0 + 1] = incl_pad - pad1; pbase[e0 + 1] = incl_pull - p1; }
+        if (e1 < E) { soff[e1 + 1] = incl_pad; pbase[e1 + 1] = incl_pull; }
+        if (tid == 0) { soff[0] = 0; pbase[0] = 0; }
+        if (g == 0) {
+            if (e0 < E) p.counts[e0] = c0;
+            if (e1 < E) p.counts[e1] = c1;
+            if (tid == (E - 1) / 2) {
+                p.scalars[0] = incl_pad;        // R_pad
+                p.scalars[1] = incl_pull;       // n_pull
+                p.scalars[2] = incl_cnt;        // N
+                p.scalars[3] = incl_pad / bm;   // n_blocks
+            }
+        }
+    }
+    __syncthreads();
+    if (g == 0)
+        for (int e = tid; e <= E; e += kGThreads) p.offsets[e] = soff[e];
+
+    // ---- this group's per-wave bases, then the stable scatter (as in route_scatter_kernel)
+    const int t0 = min(tg1, tg0 + w * kWaveTokens);
+    const int t1 = min(tg1, t0 + kWaveTokens);
+    const int l0 = (t0 - tg0) * k, l1 = (t1 - tg0) * k;
+    for (int i = l0 + lane; i < l1; i += 64)
+        if (le[i] >= 0) atomicAdd(&wh[w * E + le[i]], 1);
+    const int tt = t0 + lane;
+    const int emin = tt < t1 ? smallest_in(le, tt - tg0, k, E) : E;
+    if (emin < E) atomicAdd(&wp[w * E + emin], 1);
+    __syncthreads();
+    for (int e = tid; e < E; e += kGThreads) {
+        int run = soff[e] + gh[e], prun = pbase[e] + gp[e];
+        for (int ww = 0; ww < kGWaves; ++ww) {
+            const int c = wh[ww * E + e], cq = wp[ww * E + e];
+            wh[ww * E + e] = run;
+            wp[ww * E + e] = prun;
+            run += c;
+            prun += cq;
+        }
+    }
+    __syncthreads();
+    const int64_t hg0 = (int64_t)tg0 * k;
+    for (int base = l0; base < l1; base += 64) {
+        const int i = base + lane;
+        const int e = i < l1 ? le[i] : -1;
+        const bool valid = e >= 0;
+        const uint64_t peers = match_peers(valid, e, nbits);
+        const int64_t h = hg0 + i;
+        if (valid) {
+            const int rank = __popcll(peers & lanes_lt());
+            const int cur = wh[w * E + e];
+            const int row = cur + rank;
+            p.slot[h] = row;
+            p.row_token[row] = (int)(h / k);
+            p.row_topk[row] = (int)(h % k);
+            if (rank == 0) wh[w * E + e] = cur + __popcll(peers);
+        } else if (i < l1) {
+            p.slot[h] = -1;
+        }
+    }
+    {
+        const bool pv = emin < E;
+        const uint64_t peers = match_peers(pv, emin, nbits);
+        if (pv) {
+            const int rank = __popcll(peers & lanes_lt());
+            p.pull_order[wp[w * E + emin] + rank] = tt;
+        }
+    }
+
+    // ---- shared across workgroups: block tables and padding rows (one wave per expert), tile lists
+    const int nw_all = gridDim.x * kGWaves;
+    for (int e = g * kGWaves + w; e < E; e += nw_all) {
+        const int fill_end = soff[e] + scnt[e], end = soff[e + 1];
+        for (int q = fill_end + lane; q < end; q += 64) {
+            p.row_token[q] = -1;
+            p.row_topk[q] = -1;
+        }
+        for (int b = soff[e] / bm + lane; b < end / bm; b += 64) {
+            const int r = b * bm;
+            p.block_expert[b] = e;
+            p.slack[b] = bm - max(0, min(r + bm, fill_end) - r);
+        }
+    }
+    const int nthreads = gridDim.x * kGThreads;
+    for (int pass = 0; pass < 2; ++pass) {
+        const int nt = pass == 0 ? p.nt1 : p.nt2;
+        int32_t* tiles = pass == 0 ? p.tiles1 : p.tiles2;
+        const int total = soff[E] / bm * nt;
+        for (int l = g * kGThreads + tid; l < total; l += nthreads) {
+            int lo = 0, hi = E - 1;  // largest e whose first tile is <= l (that expert has rows)
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (soff[mid] / bm * nt <= l) lo = mid; else hi = mid - 1;
+            }
+            const int mb0 = soff[lo] / bm;
+            const int me = soff[lo + 1] / bm - mb0;
+            const int local = l - mb0 * nt;
+            tiles[2 * l] = mb0 + local % me;
+            tiles[2 * l + 1] = ((local / me) << 16) | lo;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_route(const moe_shape& s, const int64_t* topk_idx, const PlanPtrs& p, hipStream_t stream) {
     const int E = s.num_experts;
     const int64_t hits = (int64_t)s.num_tokens * s.topk;
-    if (hits <= 4096) {
-        const size_t lds = (size_t)(kWaves * E + (E + 1) + E + (E + 1) + 64) * sizeof(int32_t);
-        hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kThreads), lds, stream, topk_idx, s.num_tokens, s.topk, E,
+    if (hits <= kSingleWorkgroupHits) {
+        hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kThreads), 0, stream, topk_idx, s.num_tokens, s.topk, E,
                            s.expert_begin, s.block_m, p);
         return hipGetLastError();
     }
@@ -502,6 +655,12 @@ hipError_t launch_route(const moe_shape& s, const int64_t* topk_idx, const PlanP
     const size_t le_bytes = (size_t)kRouteTokensPerGroup * s.topk * 2;
     hipLaunchKernelGGL(route_count_kernel, dim3(groups), dim3(kGThreads), (size_t)2 * E * 4 + le_bytes, stream,
                        topk_idx, s.num_tokens, s.topk, E, s.expert_begin, groups, p.group_counts);
+    if ((int64_t)groups * E <= kFusedScanMaxWords) {
+        const size_t lds = (size_t)(2 * kGWaves * E + 5 * E + 2 + 64) * 4 + le_bytes;
+        hipLaunchKernelGGL(route_scatter_scan_kernel, dim3(groups), dim3(kGThreads), lds, stream, topk_idx,
+                           s.num_tokens, s.topk, E, s.expert_begin, groups, s.block_m, p.group_counts, p);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kThreads), (size_t)(4 * E + 2 + 64 + kScanChunkWords) * 4,
                        stream, E, s.block_m, groups, p.group_counts, p);
     hipLaunchKernelGGL(route_scatter_kernel, dim3(groups), dim3(kGThreads), (size_t)2 * kGWaves * E * 4 + le_bytes,

@@ -76,6 +76,17 @@ def test_plan_edge_cases(gpu, case):
     assert_plan_equal(g, plan_ref(ids, E, begin, bm))
 
 
+@pytest.mark.parametrize("T,k,E", [(4096, 8, 64), (4097, 8, 64), (32768, 1, 7), (32769, 1, 7), (5000, 8, 512)])
+def test_plan_path_boundary(gpu, T, k, E):
+    """Inputs just below and above the one-workgroup limit (32768 hits) take different kernels;
+    both must give the oracle's tables."""
+    rng = np.random.default_rng(T * 31 + k)
+    ids = rng.integers(-2, E + 3, size=(T, k))
+    print(f"plan path boundary: T={T} k={k} E={E} hits={T * k}", flush=True)
+    (g,) = gpu_plan(ids, E, 32, 0, gpu)
+    assert_plan_equal(g, plan_ref(ids, E, 0, 32))
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_plan_fuzz(gpu, seed):
     rng = np.random.default_rng(100 + seed)
