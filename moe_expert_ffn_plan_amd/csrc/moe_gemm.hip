@@ -48,7 +48,10 @@
 //    group 1 the activation rows.  256-column tiles (small N) use one group
 //    of four waves that reads, then multiplies.
 //  * Tiles come from a list (expert by expert; for each N-tile all M-tiles
-//    of the expert) and blockIdx is remapped so that each XCD (blockIdx % 8
+//    of the expert).  An M-tile spans up to 128 rows, several routing blocks
+//    of one expert, so a weight tile is fetched once per 128 rows rather
+//    than once per block; rows past the expert's end are masked.  blockIdx
+//    is remapped so that each XCD (blockIdx % 8
 //    on MI300-class parts) runs a contiguous run of that list: the M-tiles
 //    sharing a weight tile run together on one XCD and hit its L2.
 #include "moe_internal.h"
@@ -70,18 +73,20 @@ constexpr int kLdsBudget = 155 * 1024;  // operand ring; the rest of the 160 KiB
 
 struct GemmArgs {
     const uint8_t* a;       // Linear1: x [T, K]; Linear2: h_q [cap, K]
-    const uint8_t* a_sf;    // Linear1: x_sf [T, K/32]; Linear2: per-row-block scales [cap/BM][K/128][BM][4]
+    const uint8_t* a_sf;    // Linear1: x_sf [T, K/32]; Linear2: per-block scales [cap/bm][K/128][bm][4]
     const uint8_t* b;       // tiled weights [E][N/256][K/128][1024 x 16 B]
     const uint8_t* b_sf;    // tiled weight scales [E][N/256][K/128][256][4]
     const int32_t* scalars;
-    const int32_t* tiles;   // {m_tile, n_tile << 16 | e} per tile
+    const int32_t* tiles;   // {first row, n_tile << 16 | e, valid rows, 0} per tile
     const int32_t* row_token;
     const int32_t* row_topk;
     const float* topk_w;    // Linear1: top-k weights [T, k]
     uint8_t* out_q;         // Linear1: [cap, N/2]
-    uint8_t* out_sf;        // Linear1: per-row-block scales [cap/BM][N/256][BM][4]
+    uint8_t* out_sf;        // Linear1: per-block scales [cap/bm][N/256][bm][4]
     uint16_t* out_bf16;     // Linear2: [cap, N]
     int K, N, topk;
+    int bm_shift;           // log2 of the routing block (bm) that the scale layout uses
+    int count_idx;          // scalars[count_idx] = tiles in the list
 };
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -158,22 +163,43 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
+// A tile: rows [m, m + BM) of expert e's rows, of which the first `rows` are
+// the expert's (the rest belong to the next expert or lie past the table and
+// are neither read through nor written), columns [n * BN, n * BN + BN).
+struct TileId {
+    int m, n, e, rows;
+};
 // Tile of this workgroup: XCD-contiguous runs of the tile list.  False for
 // the padding workgroups of the grid.
-struct TileId {
-    int m, n, e;
-};
-__device__ __forceinline__ bool tile_of_block(const GemmArgs& g, int BM, int BN, TileId& t) {
-    const int total = (g.scalars[0] / BM) * (g.N / BN);
+__device__ __forceinline__ bool tile_of_block(const GemmArgs& g, TileId& t) {
+    const int total = g.scalars[g.count_idx];
     const int share = (total + kNumXcd - 1) / kNumXcd;
     const int slot = blockIdx.x / kNumXcd;
     if (slot >= share) return false;
     const int L = (blockIdx.x % kNumXcd) * share + slot;
     if (L >= total) return false;
-    t.m = g.tiles[2 * L];
-    t.n = g.tiles[2 * L + 1] >> 16;
-    t.e = g.tiles[2 * L + 1] & 0xFFFF;
+    const int32_t* e = g.tiles + kTileWords * L;
+    t.m = e[0];
+    t.n = e[1] >> 16;
+    t.e = e[1] & 0xFFFF;
+    t.rows = e[2];
     return true;
+}
+
+// Byte offset of row r's scale word of K-step 0 in the per-block layout
+// [cap/bm][KT][bm][4]; K-step kt adds kt * bm * 4.
+__device__ __forceinline__ uint32_t block_scale_offset(int r, int KT, int bm_shift) {
+    const int bm = 1 << bm_shift;
+    return (uint32_t)((((r >> bm_shift) * KT) << bm_shift) + (r & (bm - 1))) * 4u;
+}
+// The same for K-step kt of row m0 + row_local, m0 the first row of a tile:
+// without PARTIAL the tile is one block of BM rows and m0 a multiple of BM.
+template <int BM, bool PARTIAL>
+__device__ __forceinline__ uint32_t tile_scale_offset(int m0, int row_local, int KT, int kt, int bm_shift) {
+    if constexpr (PARTIAL)
+        return block_scale_offset(m0 + row_local, KT, bm_shift) + ((uint32_t)kt << (bm_shift + 2));
+    else
+        return (((uint32_t)m0 / BM * (uint32_t)KT + (uint32_t)kt) * BM + (uint32_t)row_local) * 4u;
 }
 
 // ---- operand layout of one LDS stage
@@ -209,8 +235,10 @@ struct StageDma {
     int KT, aw, anw, bw, bnw, sa_blk, sa_kt;
 
     // Linear1 gathers rows and their scales through row_token; its padding
-    // rows read token 0 (their top-k weight is 0, so they produce h = 0)
-    __device__ __forceinline__ void init_a(const GemmArgs& g, int m_tile, const int* row_tok, bool l1, int aw_,
+    // rows read token 0 (their top-k weight is 0, so they produce h = 0).
+    // Rows past the tile's valid count read token 0 (Linear1) or the tile's
+    // first row (Linear2): their results are never stored.
+    __device__ __forceinline__ void init_a(const GemmArgs& g, int m0, int rows, const int* row_tok, bool l1, int aw_,
                                            int anw_, int lane) {
         aw = aw_; anw = anw_;
         KT = g.K / kBK;
@@ -222,25 +250,24 @@ struct StageDma {
             const int c = (p & 7) ^ ((row >> 1) & 7);  // logical chunk stored in that slot
             int src_row;
             if (l1) {
-                const int t = row_tok[row];
+                const int t = row < rows ? row_tok[row] : -1;
                 src_row = t >= 0 ? t : 0;
             } else {
-                src_row = m_tile * BM + row;
+                src_row = m0 + (row < rows ? row : 0);
             }
             a_off[i] = (uint32_t)src_row * (uint32_t)g.K + (uint32_t)(c * 16);
         }
         a = g.a;
         sa_blk = aw % L::SA_INSTR;
         const int sa_row = min(sa_blk * 64 + lane, BM - 1);
+        a_sf = g.a_sf;
         if (l1) {  // x_sf [T, K/32]: the 4 bytes of K-step kt of token t sit at t * K/32 + 4 kt
-            const int t = row_tok[sa_row];
+            const int t = sa_row < rows ? row_tok[sa_row] : -1;
             sa_off = (uint32_t)(t >= 0 ? t : 0) * (uint32_t)(g.K / 32);
-            a_sf = g.a_sf;
             sa_kt = 4;
-        } else {   // per-row-block layout [cap/BM][KT][BM][4]
-            sa_off = (uint32_t)sa_row * 4;
-            a_sf = g.a_sf + (size_t)m_tile * KT * (4 * BM);
-            sa_kt = 4 * BM;
+        } else {   // per-block layout [cap/bm][KT][bm][4]
+            sa_off = block_scale_offset(m0 + (sa_row < rows ? sa_row : 0), KT, g.bm_shift);
+            sa_kt = 4 << g.bm_shift;
         }
     }
     __device__ __forceinline__ void init_b(const GemmArgs& g, const TileId& t, int bw_, int bnw_) {
@@ -336,9 +363,12 @@ __device__ __forceinline__ void mfma_step(v4f (&acc)[MI][NI], const Frags<MI, NI
 // a 64-column group, MFMA block b = ni % 4 gives lane l the output
 // 4*(l & 7) + b of the group's 32 SwiGLU channels (Linear1, gate in lanes
 // l & 8 == 0, up in the others) or 4*(l & 15) + b of its 64 columns (Linear2).
-template <int BM, int MI, int NI>
-__device__ __forceinline__ void epilogue_linear1(const v4f (&acc)[MI][NI], const GemmArgs& g, int m_tile, int wrow0,
-                                                 int gcol0, const float* row_w, const int* row_tok, int lane) {
+// PARTIAL: tiles may end before row BM (M-tiles span several routing blocks);
+// otherwise every tile has BM valid rows and the row checks compile away.
+template <int BM, int MI, int NI, bool PARTIAL>
+__device__ __forceinline__ void epilogue_linear1(const v4f (&acc)[MI][NI], const GemmArgs& g, int m0, int rows,
+                                                 int wrow0, int gcol0, const float* row_w, const int* row_tok,
+                                                 int lane) {
     static_assert(NI % 4 == 0, "a wave owns whole 64-column groups");
     const bool gate_lane = (lane & 8) == 0;
     const int j8 = lane & 7;
@@ -381,29 +411,31 @@ __device__ __forceinline__ void epilogue_linear1(const v4f (&acc)[MI][NI], const
                 int q = __builtin_amdgcn_cvt_pk_fp8_f32(h[0] * inv, h[1] * inv, 0, false);
                 q = __builtin_amdgcn_cvt_pk_fp8_f32(h[2] * inv, h[3] * inv, q, true);
                 // 32-bit offsets from uniform bases (cap * I < 2^31 is checked on the host)
-                const uint32_t row = (uint32_t)(m_tile * BM + row_local);
-                *reinterpret_cast<int*>(g.out_q + (row * (uint32_t)n_q + (uint32_t)(gcol / 2 + 4 * j8))) = q;
-                // Linear2 K-step = 256-column block of Z, byte = 64-column group within it
-                if (j8 == 0)
-                    g.out_sf[(((uint32_t)(m_tile * ksteps2 + gcol / kTileN) * BM + row_local) * 4 +
-                              (uint32_t)((gcol % kTileN) / 64))] = (uint8_t)code;
+                if (!PARTIAL || row_local < rows) {
+                    const uint32_t row = (uint32_t)(m0 + row_local);
+                    *reinterpret_cast<int*>(g.out_q + (row * (uint32_t)n_q + (uint32_t)(gcol / 2 + 4 * j8))) = q;
+                    // Linear2 K-step = 256-column block of Z, byte = 64-column group within it
+                    if (j8 == 0)
+                        g.out_sf[tile_scale_offset<BM, PARTIAL>(m0, row_local, ksteps2, gcol / kTileN, g.bm_shift) +
+                                 (uint32_t)((gcol % kTileN) / 64)] = (uint8_t)code;
+                }
             }
         }
     }
 }
 
-template <int BM, int MI, int NI>
-__device__ __forceinline__ void epilogue_linear2(const v4f (&acc)[MI][NI], const GemmArgs& g, int m_tile, int wrow0,
-                                                 int gcol0, const int* row_tok, int lane) {
+template <int BM, int MI, int NI, bool PARTIAL>
+__device__ __forceinline__ void epilogue_linear2(const v4f (&acc)[MI][NI], const GemmArgs& g, int m0, int rows,
+                                                 int wrow0, int gcol0, const int* row_tok, int lane) {
     static_assert(NI % 4 == 0, "a wave owns whole 64-column groups");
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row_local = wrow0 + mi * 16 + 4 * (lane >> 4) + i;
-            if (row_tok[row_local] < 0) continue;  // padding rows are never read
+            if ((PARTIAL && row_local >= rows) || row_tok[row_local] < 0) continue;  // padding rows are never read
             // 32-bit byte offsets from a uniform base (cap * H * 2 < 2^32)
-            const uint32_t off = ((uint32_t)(m_tile * BM + row_local) * (uint32_t)g.N +
+            const uint32_t off = ((uint32_t)(m0 + row_local) * (uint32_t)g.N +
                                   (uint32_t)(gcol0 + 4 * (lane & 15))) * 2u;
             uint8_t* out = reinterpret_cast<uint8_t*>(g.out_bf16);
 #pragma unroll
@@ -415,19 +447,20 @@ __device__ __forceinline__ void epilogue_linear2(const v4f (&acc)[MI][NI], const
         }
 }
 
-template <int BM, int MI, int NI, bool L1>
-__device__ __forceinline__ void epilogue(const v4f (&acc)[MI][NI], const GemmArgs& g, int m_tile, int wrow0,
+template <int BM, int MI, int NI, bool L1, bool PARTIAL>
+__device__ __forceinline__ void epilogue(const v4f (&acc)[MI][NI], const GemmArgs& g, const TileId& t, int wrow0,
                                          int gcol0, const float* row_w, const int* row_tok, int lane) {
-    if constexpr (L1) epilogue_linear1<BM>(acc, g, m_tile, wrow0, gcol0, row_w, row_tok, lane);
-    else epilogue_linear2<BM>(acc, g, m_tile, wrow0, gcol0, row_tok, lane);
+    if constexpr (L1) epilogue_linear1<BM, MI, NI, PARTIAL>(acc, g, t.m, t.rows, wrow0, gcol0, row_w, row_tok, lane);
+    else epilogue_linear2<BM, MI, NI, PARTIAL>(acc, g, t.m, t.rows, wrow0, gcol0, row_tok, lane);
 }
 
 template <int BM, bool L1>
-__device__ __forceinline__ void load_row_tables(const GemmArgs& g, int m_tile, float* row_w, int* row_tok, int tid) {
+__device__ __forceinline__ void load_row_tables(const GemmArgs& g, const TileId& tl, float* row_w, int* row_tok,
+                                                int tid) {
     if (tid < BM) {
-        const int t = g.row_token[m_tile * BM + tid];
+        const int t = tid < tl.rows ? g.row_token[tl.m + tid] : -1;
         row_tok[tid] = t;
-        if (L1) row_w[tid] = t >= 0 ? g.topk_w[(size_t)t * g.topk + g.row_topk[m_tile * BM + tid]] : 0.0f;
+        if (L1) row_w[tid] = t >= 0 ? g.topk_w[(size_t)t * g.topk + g.row_topk[tl.m + tid]] : 0.0f;
     }
     __syncthreads();
 }
@@ -450,7 +483,7 @@ struct Cfg4 {
     static_assert(2 * D < 64, "vmcnt range");
 };
 
-template <int BM, bool L1>
+template <int BM, bool L1, bool PARTIAL>
 __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
     using C = Cfg4<BM>;
     using L = typename C::L;
@@ -459,14 +492,14 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
     __shared__ int row_tok[BM];
 
     TileId t;
-    if (!tile_of_block(g, BM, 256, t)) return;
+    if (!tile_of_block(g, t)) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int KT = g.K / kBK;
-    load_row_tables<BM, L1>(g, t.m, row_w, row_tok, tid);
+    load_row_tables<BM, L1>(g, t, row_w, row_tok, tid);
 
     StageDma<BM, 256, C::A_PW, C::B_PW, C::SB_PW> dma;
-    dma.init_a(g, t.m, row_tok, L1, w, 4, lane);
+    dma.init_a(g, t.m, t.rows, row_tok, L1, w, 4, lane);
     dma.init_b(g, t, w, 4);
     auto issue = [&](int kt) {
         uint8_t* st = smem + (kt % L::NS) * L::STAGE;
@@ -486,7 +519,7 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
         read_frags<BM, 256>(f, smem + (kt % L::NS) * L::STAGE, wrow0, wcol0, lane);
         mfma_step(acc, f, kt == 0);
     }
-    epilogue<BM, C::MI, C::NI, L1>(acc, g, t.m, wrow0, t.n * 256 + wcol0, row_w, row_tok, lane);
+    epilogue<BM, C::MI, C::NI, L1, PARTIAL>(acc, g, t, wrow0, t.n * 256 + wcol0, row_w, row_tok, lane);
 }
 
 // ============================================================================
@@ -544,12 +577,12 @@ struct CfgPP {
 };
 constexpr int kTableSlots = 3;
 
-template <int BM, bool L1>
+template <int BM, bool L1, bool PARTIAL>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
     using C = CfgPP<BM, L1>;
     using L = typename C::L;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[L::NS * L::STAGE];
-    __shared__ int desc[kTableSlots][64];   // words 0, 1: the tile's list entry {m, n << 16 | e}
+    __shared__ int desc[kTableSlots][64];   // words 0-3: the tile's list entry
     __shared__ int meta[kTableSlots][256];  // [0, 128): row tokens; [128, 256): top-k slots
     __shared__ float wts[kTableSlots][128]; // Linear1: top-k weights of the rows
 
@@ -559,7 +592,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
     const int KT = g.K / kBK;
 
     // ---- this workgroup's tiles
-    const int total = (g.scalars[0] / BM) * (g.N / 512);
+    const int total = g.scalars[g.count_idx];
     const int share = (total + kNumXcd - 1) / kNumXcd;
     const int nslots = gridDim.x / kNumXcd;
     const int xcd = blockIdx.x % kNumXcd;
@@ -568,25 +601,28 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
     if (first >= end) return;
     const int ntiles = (end - first + nslots - 1) / nslots;
     const int S = ntiles * KT;
-    auto tile_entry = [&](int j) { return g.tiles + 2 * (first + min(j, ntiles - 1) * nslots); };
+    auto tile_entry = [&](int j) { return g.tiles + kTileWords * (first + min(j, ntiles - 1) * nslots); };
 
     // ---- table loads (one DMA instruction per wave)
     auto load_desc = [&](int j) {  // group 0
         j = min(j, ntiles - 1);
-        dma4((uint32_t)min(lane, 1) * 4, tile_entry(j), lds_addr(&desc[j % kTableSlots][0]));
+        dma4((uint32_t)min(lane, kTileWords - 1) * 4, tile_entry(j), lds_addr(&desc[j % kTableSlots][0]));
     };
-    auto load_meta = [&](int j, int m) {  // group 1; m = M-tile of tile j
+    // rows past the tile's valid count load whatever the tables hold there (the
+    // tables reserve slack rows past the last block); every reader masks them
+    auto load_meta = [&](int j, int m) {  // group 1; m = first row of tile j
         j = min(j, ntiles - 1);
         const int part = wq >> 1, half = wq & 1;
         const int row = min(half * 64 + lane, BM - 1);
-        const int32_t* src = (part == 1 ? g.row_topk : g.row_token) + (size_t)m * BM;
+        const int32_t* src = (part == 1 ? g.row_topk : g.row_token) + m;
         dma4((uint32_t)row * 4, src, lds_addr(&meta[j % kTableSlots][part * 128 + half * 64]));
     };
     auto read_entry = [&](int j, TileId& t) {
         j = min(j, ntiles - 1);
         const int a = __builtin_amdgcn_readfirstlane(desc[j % kTableSlots][0]);
         const int b = __builtin_amdgcn_readfirstlane(desc[j % kTableSlots][1]);
-        t.m = a; t.n = b >> 16; t.e = b & 0xFFFF;
+        const int r = __builtin_amdgcn_readfirstlane(desc[j % kTableSlots][2]);
+        t.m = a; t.n = b >> 16; t.e = b & 0xFFFF; t.rows = r;
     };
 
     const int wrow0 = C::SPLIT_ROWS ? grp * C::WTM : 0;
@@ -634,7 +670,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
             mfma_step<C::MI, C::NI, 0, MH>(acc, f, kt == 0);
             mfma_step<C::MI, C::NI, MH, C::MI>(acc, f, kt == 0);
             if (++kt == KT) {
-                epilogue<BM, C::MI, C::NI, L1>(acc, g, ct.m, wrow0, ct.n * 512 + wcol0, wts[ci % kTableSlots],
+                epilogue<BM, C::MI, C::NI, L1, PARTIAL>(acc, g, ct, wrow0, ct.n * 512 + wcol0, wts[ci % kTableSlots],
                                                meta[ci % kTableSlots], lane);
                 kt = 0;
                 ++ci;
@@ -642,23 +678,23 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
         }
     } else {
         StageDma<BM, 512, C::A_PW, 1, 1> dma;
-        dma.init_a(g, t0.m, meta[0], L1, wq, 4, lane);
+        dma.init_a(g, t0.m, t0.rows, meta[0], L1, wq, 4, lane);
         TileId tn;  // tile whose rows the table load fetches
         read_entry(1, tn);
         // Linear1: byte offset into topk_w of this lane's row of the issued tile
         const int w_row = min((wq & 1) * 64 + lane, BM - 1);
-        auto weight_offset = [&](int j) {
+        auto weight_offset = [&](int j, int rows) {
             const int* mt = meta[j % kTableSlots];
-            const int t = mt[w_row];
+            const int t = w_row < rows ? mt[w_row] : -1;
             return t >= 0 ? (uint32_t)(t * g.topk + mt[128 + w_row]) * 4u : 0u;
         };
-        uint32_t w_off = L1 ? weight_offset(0) : 0u;
+        uint32_t w_off = L1 ? weight_offset(0, t0.rows) : 0u;
         auto issue = [&](int s) {
             if (s % KT == 0 && s > 0) {
                 TileId t;
                 read_entry(s / KT, t);
-                dma.init_a(g, t.m, meta[(s / KT) % kTableSlots], L1, wq, 4, lane);
-                if (L1) w_off = weight_offset(s / KT);
+                dma.init_a(g, t.m, t.rows, meta[(s / KT) % kTableSlots], L1, wq, 4, lane);
+                if (L1) w_off = weight_offset(s / KT, t.rows);
             }
             dma.issue_a(smem + (s % L::NS) * L::STAGE, s % KT, lane);
             load_meta(max(s - (L::NS - 1), 0) / KT + 1, tn.m);
@@ -685,7 +721,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
             }
             mfma_step(acc, f, kt == 0);
             if (++kt == KT) {
-                epilogue<BM, C::MI, C::NI, L1>(acc, g, ct.m, wrow0, ct.n * 512 + wcol0, wts[ci % kTableSlots],
+                epilogue<BM, C::MI, C::NI, L1, PARTIAL>(acc, g, ct, wrow0, ct.n * 512 + wcol0, wts[ci % kTableSlots],
                                                meta[ci % kTableSlots], lane);
                 kt = 0;
                 ++ci;
@@ -707,7 +743,7 @@ int cu_count() {
     return c;
 }
 
-template <int BM, bool L1>
+template <int BM, bool L1, bool PARTIAL>
 hipError_t launch_bm(const GemmArgs& args, int64_t tiles, hipStream_t stream) {
     const int64_t all = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;  // one workgroup per tile
     if (gemm_bn(args.N) == 512) {
@@ -716,23 +752,32 @@ hipError_t launch_bm(const GemmArgs& args, int64_t tiles, hipStream_t stream) {
             const int64_t cus = cu_count() / kNumXcd * kNumXcd;
             grid = std::max<int64_t>(kNumXcd, std::min(all, cus));
         }
-        hipLaunchKernelGGL((gemm_pp_kernel<BM, L1>), dim3(grid), dim3(512), 0, stream, args);
+        hipLaunchKernelGGL((gemm_pp_kernel<BM, L1, PARTIAL>), dim3(grid), dim3(512), 0, stream, args);
     } else {
-        hipLaunchKernelGGL((gemm4_kernel<BM, L1>), dim3(all), dim3(256), 0, stream, args);
+        hipLaunchKernelGGL((gemm4_kernel<BM, L1, PARTIAL>), dim3(all), dim3(256), 0, stream, args);
     }
     return hipGetLastError();
 }
 
 template <bool L1>
-hipError_t launch_gemm(const GemmProblem& p, const GemmArgs& args, hipStream_t stream) {
-    const int bm = p.shape->block_m;
-    const int64_t tiles = (p.cap / bm) * (args.N / gemm_bn(args.N));  // upper bound (padded rows not yet known)
+hipError_t launch_gemm(const GemmProblem& p, GemmArgs args, hipStream_t stream) {
+    const int bm = p.shape->block_m, bmg = gemm_bm(bm);
+    args.bm_shift = 31 - __builtin_clz((unsigned)bm);
+    // upper bound on the M-tiles (the padded rows are not known yet): every M-tile but each expert's
+    // last covers bmg / bm whole blocks
+    const int64_t blocks = p.cap / bm;
+    const int64_t mtiles = std::min<int64_t>(blocks, blocks / (bmg / bm) + p.shape->num_experts);
+    const int64_t tiles = mtiles * (args.N / gemm_bn(args.N));
     if (tiles == 0) return hipSuccess;
-    switch (bm) {
-        case 16: return launch_bm<16, L1>(args, tiles, stream);
-        case 32: return launch_bm<32, L1>(args, tiles, stream);
-        case 64: return launch_bm<64, L1>(args, tiles, stream);
-        case 128: return launch_bm<128, L1>(args, tiles, stream);
+    if (bmg == bm) {
+        switch (bmg) {
+            case 16: return launch_bm<16, L1, false>(args, tiles, stream);
+            case 128: return launch_bm<128, L1, false>(args, tiles, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    switch (bmg) {
+        case 128: return launch_bm<128, L1, true>(args, tiles, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -752,6 +797,7 @@ hipError_t launch_linear1(const GemmProblem& p, const uint8_t* x, const uint8_t*
                           const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf, hipStream_t stream) {
     GemmArgs a = common_args(p);
     a.tiles = p.plan->tiles1;
+    a.count_idx = 4;
     a.topk_w = topk_w;
     a.a = x; a.a_sf = x_sf; a.b = w1; a.b_sf = w1_sf;
     a.out_q = h_q; a.out_sf = h_sf; a.out_bf16 = nullptr;
@@ -763,6 +809,7 @@ hipError_t launch_linear2(const GemmProblem& p, const uint8_t* h_q, const uint8_
                           const uint8_t* w2_sf, uint16_t* yslot, hipStream_t stream) {
     GemmArgs a = common_args(p);
     a.tiles = p.plan->tiles2;
+    a.count_idx = 5;
     a.a = h_q; a.a_sf = h_sf; a.b = w2; a.b_sf = w2_sf;
     a.out_q = nullptr; a.out_sf = nullptr; a.out_bf16 = yslot;
     a.K = p.shape->intermediate; a.N = p.shape->hidden;

@@ -24,9 +24,18 @@ constexpr int kRouteTokensPerGroup = 256;
 
 // Tile widths of the two GEMMs: 512 columns when N allows it, else 256.
 inline int gemm_bn(int n) { return n % 512 == 0 ? 512 : 256; }
+// GEMM M-tile: up to 128 rows (several block_m blocks of one expert) once block_m >= 32; for smaller
+// block_m (decode-sized batches, a block or two per expert) the tile is one block.
+inline int gemm_bm(int block_m) { return block_m >= 32 ? 128 : block_m; }
+// Rows past `cap` that the row tables reserve, so a 128-row tile starting at the last block reads
+// allocated memory (the GEMMs mask every row past the tile's valid count).
+constexpr int kRowSlack = 128;
+// Words per tile-list entry: {first row, n << 16 | e, valid rows, 0}.
+constexpr int kTileWords = 4;
 
 struct PlanLayout {
     int64_t cap = 0, max_blocks = 0, groups = 0;
+    int bmg = 0;                           // GEMM M-tile rows
     int nt1 = 0, nt2 = 0;                  // N-tiles of Linear1 (N = 2I) and Linear2 (N = H)
     int64_t max_tiles1 = 0, max_tiles2 = 0;
     size_t scalars = 0, counts = 0, offsets = 0, slot = 0, row_token = 0, row_topk = 0,
@@ -48,20 +57,22 @@ inline PlanLayout plan_layout(const moe_shape& s) {
     L.counts = take((size_t)s.num_experts * 4);
     L.offsets = take((size_t)(s.num_experts + 1) * 4);
     L.slot = take((size_t)s.num_tokens * s.topk * 4);
-    L.row_token = take((size_t)L.cap * 4);
-    L.row_topk = take((size_t)L.cap * 4);
+    L.row_token = take((size_t)(L.cap + kRowSlack) * 4);
+    L.row_topk = take((size_t)(L.cap + kRowSlack) * 4);
     L.block_expert = take((size_t)L.max_blocks * 4);
     L.slack = take((size_t)L.max_blocks * 4);
     L.pull_order = take((size_t)s.num_tokens * 4);
     L.groups = (s.num_tokens + kRouteTokensPerGroup - 1) / kRouteTokensPerGroup;
     L.group_counts = take((size_t)L.groups * s.num_experts * 2 * 4);  // hit and pull counts per group
-    // GEMM tile lists: tile = (expert, M-block, N-tile), expert by expert, for each N-tile all M-blocks
+    // GEMM tile lists: tile = (expert, M-tile, N-tile), expert by expert, for each N-tile all M-tiles;
+    // every M-tile covers at least one block, so max_blocks M-tiles bound the count
+    L.bmg = gemm_bm(s.block_m);
     L.nt1 = 2 * s.intermediate / gemm_bn(2 * s.intermediate);
     L.nt2 = s.hidden / gemm_bn(s.hidden);
     L.max_tiles1 = L.max_blocks * L.nt1;
     L.max_tiles2 = L.max_blocks * L.nt2;
-    L.tiles1 = take((size_t)L.max_tiles1 * 8);
-    L.tiles2 = take((size_t)L.max_tiles2 * 8);
+    L.tiles1 = take((size_t)L.max_tiles1 * kTileWords * 4);
+    L.tiles2 = take((size_t)L.max_tiles2 * kTileWords * 4);
     L.total = o;
     return L;
 }
@@ -85,10 +96,11 @@ inline ForwardLayout forward_layout(const moe_shape& s) {
     return F;
 }
 
+// scalars: [0] R_pad, [1] n_pull, [2] N, [3] n_blocks, [4] Linear1 tiles, [5] Linear2 tiles
 struct PlanPtrs {
     int32_t *scalars, *counts, *offsets, *slot, *row_token, *row_topk, *block_expert, *slack, *pull_order,
         *group_counts, *tiles1, *tiles2;
-    int nt1, nt2;
+    int nt1, nt2, bmg;
 };
 
 inline PlanPtrs plan_ptrs(const PlanLayout& L, void* base) {
@@ -96,7 +108,7 @@ inline PlanPtrs plan_ptrs(const PlanLayout& L, void* base) {
     auto at = [&](size_t off) { return reinterpret_cast<int32_t*>(b + off); };
     return PlanPtrs{at(L.scalars),   at(L.counts),     at(L.offsets),      at(L.slot),   at(L.row_token),
                     at(L.row_topk),  at(L.block_expert), at(L.slack),      at(L.pull_order), at(L.group_counts),
-                    at(L.tiles1),    at(L.tiles2),     L.nt1,              L.nt2};
+                    at(L.tiles1),    at(L.tiles2),     L.nt1,              L.nt2,        L.bmg};
 }
 
 // ---- launchers (each enqueues on `stream` and returns the launch status) ----

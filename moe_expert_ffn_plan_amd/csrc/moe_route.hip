@@ -73,22 +73,60 @@ __device__ int block_inclusive_scan(int v, int* scratch) {
 }
 
 
-// GEMM tile lists from the padded offsets (LDS): for a GEMM with nt N-tiles,
-// expert e's tiles start at (soff[e] / bm) * nt and run N-tile by N-tile over
-// all of e's M-blocks; entry l = {m, n << 16 | e}.
-__device__ void write_tiles(const int32_t* soff, int E, int bm, int nt, int32_t* __restrict__ tiles) {
-    const int total = soff[E] / bm * nt;
-    for (int l = threadIdx.x; l < total; l += blockDim.x) {
-        int lo = 0, hi = E - 1;  // largest e whose first tile is <= l (that expert has rows)
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (soff[mid] / bm * nt <= l) lo = mid; else hi = mid - 1;
+// GEMM tile lists from the padded offsets soff (LDS, E+1).  An M-tile covers up to bmg rows (bmg / bm
+// blocks) of one expert; expert e has ceil(blocks_e / (bmg / bm)) M-tiles, whose exclusive prefix over
+// experts goes to tb (LDS scratch, E+1).  For a GEMM with nt N-tiles, expert e's tiles start at
+// tb[e] * nt and run N-tile by N-tile over all of e's M-tiles; entry l = {first row, n << 16 | e,
+// valid rows, 0}.  Called by every thread of the workgroup; workgroup `part` of `parts` writes the
+// entries l with l / blockDim.x = part mod parts.  scalars[4], [5] = tiles of each GEMM (if `counts`).
+__device__ void write_tile_lists(const int32_t* soff, int E, int bm, int32_t* tb, const PlanPtrs& p, int part,
+                                 int parts, bool counts) {
+    const int bmg = p.bmg;
+    const int ratio = bmg / bm;  // blocks per M-tile
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        int run = 0;
+        for (int c = 0; c < E; c += 64) {
+            const int e = c + lane;
+            int v = 0;
+            if (e < E) {
+                const int nb = (soff[e + 1] - soff[e]) / bm;
+                v = (nb + ratio - 1) / ratio;
+            }
+            for (int d = 1; d < 64; d <<= 1) {
+                const int o = __shfl_up(v, d, 64);
+                if (lane >= d) v += o;
+            }
+            if (e < E) tb[e + 1] = run + v;
+            run += __shfl(v, 63, 64);
         }
-        const int mb0 = soff[lo] / bm;
-        const int me = soff[lo + 1] / bm - mb0;
-        const int local = l - mb0 * nt;
-        tiles[2 * l] = mb0 + local % me;
-        tiles[2 * l + 1] = ((local / me) << 16) | lo;
+        if (lane == 0) tb[0] = 0;
+    }
+    __syncthreads();
+    const int mt_total = tb[E];
+    if (counts && threadIdx.x == 0) {
+        p.scalars[4] = mt_total * p.nt1;
+        p.scalars[5] = mt_total * p.nt2;
+    }
+    for (int pass = 0; pass < 2; ++pass) {
+        const int nt = pass == 0 ? p.nt1 : p.nt2;
+        int32_t* tiles = pass == 0 ? p.tiles1 : p.tiles2;
+        const int total = mt_total * nt;
+        for (int l = part * blockDim.x + threadIdx.x; l < total; l += parts * blockDim.x) {
+            int lo = 0, hi = E - 1;  // largest e whose first tile is <= l (that expert has rows)
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (tb[mid] * nt <= l) lo = mid; else hi = mid - 1;
+            }
+            const int me = tb[lo + 1] - tb[lo];
+            const int local = l - tb[lo] * nt;
+            const int m0 = soff[lo] + (local % me) * bmg;
+            int32_t* t = tiles + (size_t)kTileWords * l;
+            t[0] = m0;
+            t[1] = ((local / me) << 16) | lo;
+            t[2] = min(bmg, soff[lo + 1] - m0);
+            t[3] = 0;
+        }
     }
 }
 
@@ -105,6 +143,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
     __shared__ int32_t soff[kMaxExperts + 1];      // padded offsets
     __shared__ int32_t scnt[kMaxExperts];          // counts (later pull counts)
     __shared__ int32_t sbase[kMaxExperts + 1];     // pull-order bases
+    __shared__ int32_t tb[kMaxExperts + 1];        // M-tile bases per expert
     __shared__ int32_t scratch[64];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
@@ -208,8 +247,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
             p.row_topk[q] = -1;
         }
     }
-    write_tiles(soff, E, bm, p.nt1, p.tiles1);
-    write_tiles(soff, E, bm, p.nt2, p.tiles2);
+    write_tile_lists(soff, E, bm, tb, p, 0, 1, true);
     __syncthreads();
 
     // ---- pass 5: pull order = tokens with a hit, by smallest local expert, then t
@@ -335,7 +373,8 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(int E, int bm, int
     int32_t* pbase = scnt + E;      // [E+1] pull bases
     int32_t* ptot = pbase + E + 1;  // [E] pull counts
     int32_t* scratch = ptot + E;    // [64]
-    int32_t* chunk = scratch + 64;  // [kScanChunkWords]
+    int32_t* tb = scratch + 64;     // [E+1] M-tile bases
+    int32_t* chunk = tb + E + 1;    // [kScanChunkWords]
     const int tid = threadIdx.x;
     const int gpc = max(1, kScanChunkWords / (2 * E));  // groups per chunk
     const bool one_chunk = groups <= gpc;               // then the group prefixes stay in LDS
@@ -420,8 +459,7 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(int E, int bm, int
             p.row_topk[q] = -1;
         }
     }
-    write_tiles(soff, E, bm, p.nt1, p.tiles1);
-    write_tiles(soff, E, bm, p.nt2, p.tiles2);
+    write_tile_lists(soff, E, bm, tb, p, 0, 1, true);
 }
 
 __global__ __launch_bounds__(kGThreads) void route_scatter_kernel(const int64_t* __restrict__ ids, int T, int k, int E,
@@ -506,7 +544,8 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int
     int32_t* gh = pbase + E + 1;            // [E] this group's first row of each expert (before soff)
     int32_t* gp = gh + E;                   // [E] this group's first pull position (before pbase)
     int32_t* scratch = gp + E;              // [64]
-    int16_t* le = reinterpret_cast<int16_t*>(scratch + 64);  // [256 * k]
+    int32_t* tb = scratch + 64;             // [E+1] M-tile bases
+    int16_t* le = reinterpret_cast<int16_t*>(tb + E + 1);  // [256 * k]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = blockIdx.x;
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     for (int i = tid; i < 2 * kGWaves * E; i += kGThreads) lds[i] = 0;
@@ -621,24 +660,7 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int
             p.slack[b] = bm - max(0, min(r + bm, fill_end) - r);
         }
     }
-    const int nthreads = gridDim.x * kGThreads;
-    for (int pass = 0; pass < 2; ++pass) {
-        const int nt = pass == 0 ? p.nt1 : p.nt2;
-        int32_t* tiles = pass == 0 ? p.tiles1 : p.tiles2;
-        const int total = soff[E] / bm * nt;
-        for (int l = g * kGThreads + tid; l < total; l += nthreads) {
-            int lo = 0, hi = E - 1;  // largest e whose first tile is <= l (that expert has rows)
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (soff[mid] / bm * nt <= l) lo = mid; else hi = mid - 1;
-            }
-            const int mb0 = soff[lo] / bm;
-            const int me = soff[lo + 1] / bm - mb0;
-            const int local = l - mb0 * nt;
-            tiles[2 * l] = mb0 + local % me;
-            tiles[2 * l + 1] = ((local / me) << 16) | lo;
-        }
-    }
+    write_tile_lists(soff, E, bm, tb, p, g, gridDim.x, g == 0);
 }
 
 }  // namespace
@@ -656,12 +678,12 @@ hipError_t launch_route(const moe_shape& s, const int64_t* topk_idx, const PlanP
     hipLaunchKernelGGL(route_count_kernel, dim3(groups), dim3(kGThreads), (size_t)2 * E * 4 + le_bytes, stream,
                        topk_idx, s.num_tokens, s.topk, E, s.expert_begin, groups, p.group_counts);
     if ((int64_t)groups * E <= kFusedScanMaxWords) {
-        const size_t lds = (size_t)(2 * kGWaves * E + 5 * E + 2 + 64) * 4 + le_bytes;
+        const size_t lds = (size_t)(2 * kGWaves * E + 6 * E + 3 + 64) * 4 + le_bytes;
         hipLaunchKernelGGL(route_scatter_scan_kernel, dim3(groups), dim3(kGThreads), lds, stream, topk_idx,
                            s.num_tokens, s.topk, E, s.expert_begin, groups, s.block_m, p.group_counts, p);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kThreads), (size_t)(4 * E + 2 + 64 + kScanChunkWords) * 4,
+    hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kThreads), (size_t)(5 * E + 3 + 64 + kScanChunkWords) * 4,
                        stream, E, s.block_m, groups, p.group_counts, p);
     hipLaunchKernelGGL(route_scatter_kernel, dim3(groups), dim3(kGThreads), (size_t)2 * kGWaves * E * 4 + le_bytes,
                        stream, topk_idx, s.num_tokens, s.topk, E, s.expert_begin, groups, p.group_counts, p);
