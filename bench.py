@@ -180,7 +180,10 @@ def main() -> int:
     tflops = useful / (ms * 1e-3) / 1e12
     l1_flops = 2.0 * n_valid * 2 * I * H
     l1_tflops = l1_flops / (l1_ms * 1e-3) / 1e12
-    kname = ("gemm_pp_kernel<%d, true>" if (2 * I) % 512 == 0 else "gemm4_kernel<%d, true>") % w.block_m
+    # GEMM M-tile: 128 rows (several routing blocks of one expert) from block_m 32 up, else one block
+    bmg = 128 if w.block_m >= 32 else w.block_m
+    kname = "%s<%d, true, %s>" % ("gemm_pp_kernel" if (2 * I) % 512 == 0 else "gemm4_kernel", bmg,
+                                  "true" if w.block_m < bmg else "false")
     roofline = {"kernel": f"Linear1 grouped GEMM ({kname})", "bound": "mfma", "achieved": round(l1_tflops, 2),
                 "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(l1_tflops / PEAK_MFMA_TFLOPS, 4),
                 "traffic": linear1_traffic(w.name)}
