@@ -6,9 +6,12 @@
 One step = the whole hot path on one batch of synthetic input already resident
 in HBM: routing tables (moe_plan), grouped Linear1 with the fused
 SwiGLU/requant epilogue, grouped Linear2, and the top-k combine, enqueued on
-one stream.  The four stages are the same calls moe_forward makes; they are
-issued one by one so HIP events on that stream can bracket the Linear1 kernel
-inside the timed steps (the roofline's achieved rate).  Three copies of the
+one stream.  The stages are the calls moe_forward makes (moe_plan,
+moe_expert_ffn, both GEMMs in one persistent launch, for block_m < 128, else
+moe_linear1 and moe_linear2; moe_combine); they are issued one by one so HIP
+events on that stream can bracket the dominant GEMM launch inside the timed
+steps (the roofline's achieved rate).  --staged and --expert-ffn force one
+schedule or the other.  Three copies of the
 expert weights are rotated between steps so they stream from HBM rather than
 the 256 MB Infinity Cache.  The default warmup (50 steps) lets the clocks
 settle; the first steps after idle run ~15% slower.
@@ -36,10 +39,11 @@ PEAK_MFMA_TFLOPS = 5000.0      # MI355X dense FP8 MFMA; FP8 x FP4 scaled MFMA is
 PEAK_HBM_GBS = 8000.0
 
 
-def linear1_traffic(workload: str):
-    """HBM bytes per Linear1 launch from the committed rocprofv3 byte-counter summary, when it was taken on
-    this workload with the current GEMM source (its sha256 is recorded there); else None."""
-    path = os.path.join(ROOT, "profiles", f"linear1_gemm_{workload}_traffic.md")
+def kernel_traffic(kind: str, workload: str):
+    """HBM bytes per launch of the dominant GEMM kernel (kind: expert_ffn or linear1) from the committed
+    rocprofv3 byte-counter summary, when it was taken on this workload with the current GEMM source (its
+    sha256 is recorded there); else None."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_gemm_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -89,6 +93,10 @@ def main() -> int:
     ap.add_argument("--weight-copies", type=int, default=3)
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--staged", action="store_true",
+                    help="run Linear1 and Linear2 as two launches (moe_linear1, moe_linear2) for every shape")
+    ap.add_argument("--expert-ffn", action="store_true",
+                    help="run Linear1 and Linear2 through moe_expert_ffn (one launch) wherever it is supported")
     ap.add_argument("--host-inputs", action="store_true",
                     help="draw the synthetic inputs on the CPU and copy them (fewer torch GPU kernels, for profilers)")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -132,24 +140,36 @@ def main() -> int:
     ws = torch.empty(B.forward_workspace_bytes(s), dtype=torch.uint8, device=dev)
     y = torch.empty(w.num_tokens, w.hidden, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
-    stages = ["plan", "linear1", "linear2", "combine"]
+    # the schedule moe_forward picks: moe_expert_ffn (one persistent launch where the shape allows) for
+    # block_m < 128, else the two GEMM launches
+    fused = B.forward_uses_expert_ffn(s) and B.expert_ffn_is_fused(s) and not args.staged
+    if args.expert_ffn:
+        fused = B.expert_ffn_is_fused(s)
+    stages = ["plan", "expert_ffn", "combine"] if fused else ["plan", "linear1", "linear2", "combine"]
 
-    def step(i, events=None, l1_events=None):
+    def step(i, events=None, k_events=None, staged=not fused):
+        """One step; events: one per stage boundary; k_events: around the dominant GEMM launch."""
         wt = weights[i % len(weights)]
         rec = (lambda j: events[j].record(stream)) if events is not None else (lambda j: None)
         rec(0)
         B.plan(s, d["topk_idx"], plan_ws, stream)
         rec(1)
-        if l1_events is not None:
-            l1_events[0].record(stream)
-        B.linear1(s, d["x"], d["x_sf"], d["topk_w"], wt["w1"], wt["w1_sf"], plan_ws, ws, stream)
-        if l1_events is not None:
-            l1_events[1].record(stream)
-        rec(2)
-        B.linear2(s, wt["w2"], wt["w2_sf"], plan_ws, ws, stream)
-        rec(3)
+        if k_events is not None:
+            k_events[0].record(stream)
+        if staged:
+            B.linear1(s, d["x"], d["x_sf"], d["topk_w"], wt["w1"], wt["w1_sf"], plan_ws, ws, stream)
+            if k_events is not None:
+                k_events[1].record(stream)
+            rec(2)
+            B.linear2(s, wt["w2"], wt["w2_sf"], plan_ws, ws, stream)
+        else:
+            B.expert_ffn(s, d["x"], d["x_sf"], d["topk_w"], wt["w1"], wt["w1_sf"], wt["w2"], wt["w2_sf"], plan_ws,
+                         ws, stream)
+            if k_events is not None:
+                k_events[1].record(stream)
+        rec(3 if staged else 2)
         B.combine(s, plan_ws, ws, y, stream)
-        rec(4)
+        rec(4 if staged else 3)
 
     for i in range(args.warmup):
         step(i)
@@ -157,36 +177,45 @@ def main() -> int:
     scal = B.plan_view(s, plan_ws)["scalars"].cpu().tolist()
     r_pad, n_valid = scal[0], scal[2]
 
-    # timed steps: wall time; HIP events bracket only the Linear1 kernel (same stream)
-    l1_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # timed steps: wall time; HIP events bracket only the dominant GEMM launch (same stream)
+    k_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, l1_events=l1_evs[i])
+        step(i, k_events=k_evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
-    l1_ms = sum(e[0].elapsed_time(e[1]) for e in l1_evs) / args.steps
+    k_ms = sum(e[0].elapsed_time(e[1]) for e in k_evs) / args.steps
 
-    # untimed breakdown pass: an event between every stage
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    kern_ms = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, name in enumerate(stages)}
+    # untimed breakdown passes: an event between every stage (and the two-launch path for comparison)
+    def breakdown(staged):
+        names = ["plan", "linear1", "linear2", "combine"] if staged else stages
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            step(i, evs[i], staged=staged)
+        torch.cuda.synchronize()
+        return {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, name in enumerate(names)}
+    kern_ms = breakdown(not fused)
+    staged_ms = breakdown(True) if fused else None
 
     H, I = w.hidden, w.intermediate
     useful = 2.0 * n_valid * 3 * H * I
     tflops = useful / (ms * 1e-3) / 1e12
-    l1_flops = 2.0 * n_valid * 2 * I * H
-    l1_tflops = l1_flops / (l1_ms * 1e-3) / 1e12
     # GEMM M-tile: 128 rows (several routing blocks of one expert) from block_m 32 up, else one block
     bmg = 128 if w.block_m >= 32 else w.block_m
-    kname = "%s<%d, true, %s>" % ("gemm_pp_kernel" if (2 * I) % 512 == 0 else "gemm4_kernel", bmg,
-                                  "true" if w.block_m < bmg else "false")
-    roofline = {"kernel": f"Linear1 grouped GEMM ({kname})", "bound": "mfma", "achieved": round(l1_tflops, 2),
-                "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(l1_tflops / PEAK_MFMA_TFLOPS, 4),
-                "traffic": linear1_traffic(w.name)}
+    partial = "true" if w.block_m < bmg else "false"
+    if fused:
+        k_flops = useful
+        kname = f"Linear1 + Linear2 in one launch (gemm_fused_kernel<{bmg}, {partial}>)"
+    else:
+        k_flops = 2.0 * n_valid * 2 * I * H
+        kname = "Linear1 grouped GEMM (%s<%d, true, %s>)" % (
+            "gemm_pp_kernel" if (2 * I) % 512 == 0 else "gemm4_kernel", bmg, partial)
+    k_tflops = k_flops / (k_ms * 1e-3) / 1e12
+    roofline = {"kernel": kname, "bound": "mfma", "achieved": round(k_tflops, 2),
+                "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_MFMA_TFLOPS, 4),
+                "traffic": kernel_traffic("expert_ffn" if fused else "linear1", w.name)}
     out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "fp8e4m3 x fp4e2m1 (fp32 accumulate)", "data": "synthetic",
@@ -195,9 +224,11 @@ def main() -> int:
                       "valid_rows": n_valid, "padded_rows": r_pad, "weight_copies": args.weight_copies},
            "tokens_per_s": round(w.num_tokens / (ms * 1e-3), 1),
            "pct_of_mfma_peak": round(100 * tflops / PEAK_MFMA_TFLOPS, 2),
-           "linear1_ms": round(l1_ms, 4),
+           "gemm_ms": round(k_ms, 4),
            "kernel_ms": {k: round(v, 4) for k, v in kern_ms.items()},
            "roofline": roofline}
+    if staged_ms is not None:
+        out["staged_kernel_ms"] = {k: round(v, 4) for k, v in staged_ms.items()}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, d, args.cpu_sample_tokens)
     print(json.dumps(out), flush=True)

@@ -186,13 +186,18 @@ MOE_API int moe_forward(const moe_shape* shape,
                 const void* plan_ws,
                 void* ws, size_t ws_bytes, void* stream);
 
-/* ---- the forward's stages, one kernel each (Linear1 gathers its rows, their
- * scales and the top-k weights through the plan's row tables itself) -------
- * moe_forward(plan_ws != NULL) is exactly moe_linear1, moe_linear2 and
- * moe_combine in this order on one stream; they are exposed so a caller can
- * schedule or time the stages itself.  Arguments mean what they mean for
- * moe_forward; plan_ws (from moe_plan) is required here, and ws must be the
- * same forward workspace for all three.
+/* ---- the forward's stages (Linear1 gathers its rows, their scales and the
+ * top-k weights through the plan's row tables itself) ------------------------
+ * moe_forward(plan_ws != NULL) is exactly moe_expert_ffn (for block_m < 128)
+ * or moe_linear1 then moe_linear2 (block_m = 128), then moe_combine, in this
+ * order on one stream; moe_expert_ffn computes what moe_linear1 then
+ * moe_linear2 compute (bit for bit), in one persistent launch where the
+ * shape allows it.  (Small routing blocks mean few rows per expert and few
+ * tiles per CU, where the single launch saves a kernel tail and ramp; with
+ * many tiles per CU it measured slightly slower.)  They are exposed so a
+ * caller can schedule or time the stages itself.  Arguments mean what they mean for moe_forward; plan_ws
+ * (from moe_plan) is required here, and ws must be the same forward
+ * workspace for all of them.
  *   moe_linear1: grouped Linear1 over the routing layout with the fused
  *     SwiGLU x top-k weight and FP8 requant epilogue -> h_q, h_sf in ws
  *     (reading notes "stage three" and "stage four").
@@ -210,6 +215,25 @@ MOE_API int moe_linear2(const moe_shape* shape,
 MOE_API int moe_combine(const moe_shape* shape, const void* plan_ws,
                 const void* ws, size_t ws_bytes, uint16_t* y, void* stream);
 
+/* Linear1 and Linear2 in one persistent launch: the single-launch schedule of
+ * the reading notes (execution path, item 6, and "stage two": Linear2 blocks
+ * wait on arrival marks set by the Linear1 epilogue; walk-through section
+ * 4.3).  One workgroup per CU runs its Linear1 tiles, then its Linear2 tiles;
+ * a Linear2 tile starts once every Linear1 tile of its rows has stored them.
+ * Used when 2I and H are multiples of 512, both K-loops are long enough for
+ * the persistent kernel (H/128 and I/128 >= 4 for block_m >= 32, >= 6 for
+ * block_m 16) and 2I/512 <= 64; otherwise this is moe_linear1 + moe_linear2.
+ * The completion flags live in ws (any initial contents: each launch stamps
+ * them with a fresh epoch); calls sharing a ws must not overlap.  A Linear2
+ * tile that waits for about half a second gives up and sets the forward view's
+ * sync_status to 1 (it needs every workgroup of the launch resident at once;
+ * the library never clears the word). */
+MOE_API int moe_expert_ffn(const moe_shape* shape,
+                const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
+                const uint8_t* w1, const uint8_t* w1_sf,
+                const uint8_t* w2, const uint8_t* w2_sf,
+                const void* plan_ws, void* ws, size_t ws_bytes, void* stream);
+
 /* Device pointers to the intermediates inside a forward workspace, for
  * tests (no GPU work):
  *   h_q   uint8  [cap, I]     FP8 E4M3 Linear2 input (SwiGLU x w, requantised)
@@ -218,6 +242,8 @@ MOE_API int moe_combine(const moe_shape* shape, const void* plan_ws,
  *         [r / block_m][g / 4][r % block_m][g % 4]
  *   yslot uint16 [cap, H]     BF16 Linear2 output per slot row
  *   plan  the plan region used when moe_forward got plan_ws == NULL
+ *   sync_status  uint32 word set to 1 when a moe_expert_ffn launch gave up
+ *         waiting (see there)
  * Rows of padding (and rows >= R_pad) hold unspecified values. */
 typedef struct moe_forward_view {
     uint8_t* h_q;
@@ -225,6 +251,7 @@ typedef struct moe_forward_view {
     uint16_t* yslot;
     void* plan;
     int64_t capacity_rows;
+    uint32_t* sync_status;
 } moe_forward_view;
 MOE_API int moe_forward_view_get(const moe_shape* shape, void* ws, moe_forward_view* out);
 

@@ -38,14 +38,14 @@ class PlanView(ctypes.Structure):
 
 class ForwardView(ctypes.Structure):
     _fields_ = [("h_q", ctypes.c_void_p), ("h_sf", ctypes.c_void_p), ("yslot", ctypes.c_void_p),
-                ("plan", ctypes.c_void_p), ("capacity_rows", ctypes.c_int64)]
+                ("plan", ctypes.c_void_p), ("capacity_rows", ctypes.c_int64), ("sync_status", ctypes.c_void_p)]
 
 
 _lib = None
 
 EXPORTS = ["moe_capacity_rows", "moe_plan_workspace_bytes", "moe_plan", "moe_plan_view_get",
            "moe_forward_workspace_bytes", "moe_forward", "moe_linear1", "moe_linear2", "moe_combine",
-           "moe_prepare_weights",
+           "moe_expert_ffn", "moe_prepare_weights",
            "moe_forward_view_get", "moe_device_supported", "moe_status_str"]
 
 
@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
         L.moe_linear1.argtypes = [S, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_linear2.argtypes = [S, VP, VP, VP, VP, SZ, VP]
         L.moe_combine.argtypes = [S, VP, VP, SZ, VP, VP]
+        L.moe_expert_ffn.argtypes = [S, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_forward_view_get.argtypes = [S, VP, P(ForwardView)]
         L.moe_device_supported.argtypes = [ctypes.c_int]
         L.moe_status_str.argtypes = [ctypes.c_int]
@@ -218,6 +219,32 @@ def linear2(shape: MoeShape, w2, w2_sf, plan_ws, ws, stream=None) -> None:
     _check("moe_linear2", st)
 
 
+def expert_ffn(shape: MoeShape, x, x_sf, topk_w, w1, w1_sf, w2, w2_sf, plan_ws, ws, stream=None) -> None:
+    T, H, I, E, k = shape.num_tokens, shape.hidden, shape.intermediate, shape.num_experts, shape.topk
+    dev, u8 = ws.device, torch.uint8
+    st = lib().moe_expert_ffn(ctypes.byref(shape), _ptr(x, u8, "x", dev, T * H),
+                              _ptr(x_sf, u8, "x_sf", dev, T * H // 32), _ptr(topk_w, torch.float32, "topk_w", dev, T * k),
+                              _ptr(w1, u8, "w1", dev, E * 2 * I * H // 2),
+                              _ptr(w1_sf, u8, "w1_sf", dev, E * 2 * I * H // 32),
+                              _ptr(w2, u8, "w2", dev, E * H * I // 2), _ptr(w2_sf, u8, "w2_sf", dev, E * H * I // 32),
+                              _ptr(plan_ws, u8, "plan_ws", dev), _ptr(ws, u8, "ws"), ws.numel(), _stream(stream))
+    _check("moe_expert_ffn", st)
+
+
+def expert_ffn_is_fused(shape: MoeShape) -> bool:
+    """Whether moe_expert_ffn runs as one persistent launch for this shape (the rule stated in moe.h)."""
+    min_kt = 6 if shape.block_m < 32 else 4
+    two_i, h = 2 * shape.intermediate, shape.hidden
+    return (two_i % 512 == 0 and h % 512 == 0 and two_i // 512 <= 64 and h // 128 >= min_kt
+            and shape.intermediate // 128 >= min_kt)
+
+
+def forward_uses_expert_ffn(shape: MoeShape) -> bool:
+    """Whether moe_forward runs the GEMMs through moe_expert_ffn (block_m < 128) or as moe_linear1 +
+    moe_linear2 (the rule stated in moe.h)."""
+    return shape.block_m < 128
+
+
 def combine(shape: MoeShape, plan_ws, ws, y, stream=None) -> None:
     dev = ws.device
     yv = y.view(torch.int16) if y.dtype == torch.bfloat16 else y
@@ -256,4 +283,5 @@ def forward_view(shape: MoeShape, ws: torch.Tensor) -> dict:
     return {"h_q": _slice(ws, v.h_q, torch.uint8, cap * I).view(cap, I),
             "h_sf": untile_row_scales(_slice(ws, v.h_sf, torch.uint8, cap * I // 32), cap, I, shape.block_m),
             "yslot": _slice(ws, v.yslot, torch.int16, cap * H).view(cap, H),
-            "plan_ws": ws[plan_off:], "capacity_rows": cap}
+            "plan_ws": ws[plan_off:], "capacity_rows": cap,
+            "sync_status": _slice(ws, v.sync_status, torch.int32, 1)}

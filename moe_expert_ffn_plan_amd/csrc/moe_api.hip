@@ -121,6 +121,7 @@ int moe_forward_view_get(const moe_shape* shape, void* ws, moe_forward_view* out
     out->yslot = reinterpret_cast<uint16_t*>(b + F.yslot);
     out->plan = b + F.plan_base;
     out->capacity_rows = F.plan.cap;
+    out->sync_status = reinterpret_cast<uint32_t*>(b + F.status);
     return MOE_OK;
 }
 
@@ -195,6 +196,30 @@ int moe_linear2(const moe_shape* shape, const uint8_t* w2, const uint8_t* w2_sf,
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+int moe_expert_ffn(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
+                   const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2, const uint8_t* w2_sf,
+                   const void* plan_ws, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->num_tokens == 0) return MOE_OK;
+    if (!x || !x_sf || !topk_w || !w1 || !w1_sf || !w2 || !w2_sf || !plan_ws || !ws) return MOE_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(x_sf, 16) || !aligned(w1, 16) || !aligned(w1_sf, 16) || !aligned(w2, 16) ||
+        !aligned(w2_sf, 16) || !aligned(topk_w, 4) || !aligned(ws, kAlign) || !aligned(plan_ws, kAlign))
+        return MOE_ERR_ALIGN;
+    const ForwardLayout F = forward_layout(*shape);
+    if (ws_bytes < F.total) return MOE_ERR_WORKSPACE;
+    if ((st = check_arch_current()) != MOE_OK) return st;
+    const PlanPtrs p = plan_ptrs(F.plan, const_cast<void*>(plan_ws));
+    char* base = static_cast<char*>(ws);
+    const GemmProblem g{shape, &p, F.plan.cap};
+    const hipError_t e = launch_expert_ffn(
+        g, x, x_sf, topk_w, w1, w1_sf, reinterpret_cast<uint8_t*>(base + F.h_q),
+        reinterpret_cast<uint8_t*>(base + F.h_sf), w2, w2_sf, reinterpret_cast<uint16_t*>(base + F.yslot),
+        reinterpret_cast<uint32_t*>(base + F.flags), reinterpret_cast<uint32_t*>(base + F.status),
+        static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 int moe_combine(const moe_shape* shape, const void* plan_ws, const void* ws, size_t ws_bytes, uint16_t* y,
                 void* stream) {
     int st = check_shape(shape);
@@ -234,8 +259,15 @@ int moe_forward(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, c
                                           static_cast<hipStream_t>(stream));
         if (e != hipSuccess) return MOE_ERR_HIP;
     }
-    if ((st = moe_linear1(shape, x, x_sf, topk_w, w1, w1_sf, plan, ws, ws_bytes, stream)) != MOE_OK) return st;
-    if ((st = moe_linear2(shape, w2, w2_sf, plan, ws, ws_bytes, stream)) != MOE_OK) return st;
+    // one persistent launch for small routing blocks (few tiles per CU, where the second launch's ramp
+    // and the first one's tail show), two launches otherwise
+    if (shape->block_m < 128) {
+        if ((st = moe_expert_ffn(shape, x, x_sf, topk_w, w1, w1_sf, w2, w2_sf, plan, ws, ws_bytes, stream)) != MOE_OK)
+            return st;
+    } else {
+        if ((st = moe_linear1(shape, x, x_sf, topk_w, w1, w1_sf, plan, ws, ws_bytes, stream)) != MOE_OK) return st;
+        if ((st = moe_linear2(shape, w2, w2_sf, plan, ws, ws_bytes, stream)) != MOE_OK) return st;
+    }
     return moe_combine(shape, plan, ws, ws_bytes, y, stream);
 }
 

@@ -58,6 +58,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <random>
 
 namespace moe {
 namespace {
@@ -77,7 +78,7 @@ struct GemmArgs {
     const uint8_t* b;       // tiled weights [E][N/256][K/128][1024 x 16 B]
     const uint8_t* b_sf;    // tiled weight scales [E][N/256][K/128][256][4]
     const int32_t* scalars;
-    const int32_t* tiles;   // {first row, n_tile << 16 | e, valid rows, 0} per tile
+    const int32_t* tiles;   // {first row, n_tile << 16 | e, valid rows, M-tile index} per tile
     const int32_t* row_token;
     const int32_t* row_topk;
     const float* topk_w;    // Linear1: top-k weights [T, k]
@@ -128,6 +129,24 @@ __device__ __forceinline__ float max8(float v) {
 
 // ---- LDS DMA: lane l reads `size` bytes at the wave-uniform base plus its
 // own 32-bit offset and writes them at LDS address m0 + l * size.
+// The base must be wave-uniform; the compiler cannot always prove that of a
+// pointer picked at run time from one of two argument blocks, so it is read
+// from the first lane (free where it already sits in SGPRs).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+// Lane index computed where it is used.  Code that runs once per tile takes
+// it from here so the compiler recomputes the per-lane values it derives
+// (two instructions) instead of keeping them live across the K-loop, where
+// the registers are needed for fragments and accumulators.
+__device__ __forceinline__ int fresh_lane() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
     asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
@@ -167,22 +186,34 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // the expert's (the rest belong to the next expert or lie past the table and
 // are neither read through nor written), columns [n * BN, n * BN + BN).
 struct TileId {
-    int m, n, e, rows;
+    int m, n, e, rows, mt;  // mt: M-tile index over all experts
 };
-// Tile of this workgroup: XCD-contiguous runs of the tile list.  False for
-// the padding workgroups of the grid.
-__device__ __forceinline__ bool tile_of_block(const GemmArgs& g, TileId& t) {
-    const int total = g.scalars[g.count_idx];
-    const int share = (total + kNumXcd - 1) / kNumXcd;
-    const int slot = blockIdx.x / kNumXcd;
-    if (slot >= share) return false;
-    const int L = (blockIdx.x % kNumXcd) * share + slot;
-    if (L >= total) return false;
+// XCD xcd's part of a tile list with nt tiles per M-tile (the list runs
+// M-tile by M-tile): the tiles of M-tiles [xcd * s, (xcd + 1) * s), s =
+// ceil(M-tiles / 8), as list range [begin, end).  Both GEMMs' lists split
+// into the same M-tiles, so an XCD's Linear2 tiles need only the rows its own
+// Linear1 tiles computed, and the tiles sharing a weight tile (the M-tiles of
+// one expert) run together on one XCD and hit its L2.
+__device__ __forceinline__ void xcd_chunk(const GemmArgs& g, int nt, int xcd, int& begin, int& end) {
+    const int mts = g.scalars[g.count_idx] / nt;
+    const int share = (mts + kNumXcd - 1) / kNumXcd;
+    begin = min(xcd * share, mts) * nt;
+    end = min((xcd + 1) * share, mts) * nt;
+}
+
+// Tile of this workgroup (one tile per workgroup, blockIdx % 8 = XCD).
+// False for the padding workgroups of the grid.
+__device__ __forceinline__ bool tile_of_block(const GemmArgs& g, int BN, TileId& t) {
+    int begin, end;
+    xcd_chunk(g, g.N / BN, blockIdx.x % kNumXcd, begin, end);
+    const int L = begin + blockIdx.x / kNumXcd;
+    if (L >= end) return false;
     const int32_t* e = g.tiles + kTileWords * L;
     t.m = e[0];
     t.n = e[1] >> 16;
     t.e = e[1] & 0xFFFF;
     t.rows = e[2];
+    t.mt = e[3];
     return true;
 }
 
@@ -239,7 +270,8 @@ struct StageDma {
     // Rows past the tile's valid count read token 0 (Linear1) or the tile's
     // first row (Linear2): their results are never stored.
     __device__ __forceinline__ void init_a(const GemmArgs& g, int m0, int rows, const int* row_tok, bool l1, int aw_,
-                                           int anw_, int lane) {
+                                           int anw_) {
+        const int lane = fresh_lane();
         aw = aw_; anw = anw_;
         KT = g.K / kBK;
 #pragma unroll
@@ -257,10 +289,10 @@ struct StageDma {
             }
             a_off[i] = (uint32_t)src_row * (uint32_t)g.K + (uint32_t)(c * 16);
         }
-        a = g.a;
+        a = static_cast<const uint8_t*>(uniform_ptr(g.a));
         sa_blk = aw % L::SA_INSTR;
         const int sa_row = min(sa_blk * 64 + lane, BM - 1);
-        a_sf = g.a_sf;
+        a_sf = static_cast<const uint8_t*>(uniform_ptr(g.a_sf));
         if (l1) {  // x_sf [T, K/32]: the 4 bytes of K-step kt of token t sit at t * K/32 + 4 kt
             const int t = sa_row < rows ? row_tok[sa_row] : -1;
             sa_off = (uint32_t)(t >= 0 ? t : 0) * (uint32_t)(g.K / 32);
@@ -275,8 +307,8 @@ struct StageDma {
         KT = g.K / kBK;
         const int tn0 = t.n * (BN / kTileN);  // first 256-column block of this tile
         const size_t tb0 = ((size_t)t.e * (g.N / kTileN) + tn0) * KT;
-        b = g.b + tb0 * 16 * 1024;
-        b_sf = g.b_sf + tb0 * 256 * 4;
+        b = static_cast<const uint8_t*>(uniform_ptr(g.b + tb0 * 16 * 1024));
+        b_sf = static_cast<const uint8_t*>(uniform_ptr(g.b_sf + tb0 * 256 * 4));
     }
     __device__ __forceinline__ void issue_a(uint8_t* st, int kt, int lane) const {
 #pragma unroll
@@ -365,7 +397,9 @@ __device__ __forceinline__ void mfma_step(v4f (&acc)[MI][NI], const Frags<MI, NI
 // l & 8 == 0, up in the others) or 4*(l & 15) + b of its 64 columns (Linear2).
 // PARTIAL: tiles may end before row BM (M-tiles span several routing blocks);
 // otherwise every tile has BM valid rows and the row checks compile away.
-template <int BM, int MI, int NI, bool PARTIAL>
+// COHERENT: the stores are device-scope (sc1) stores, complete at device scope
+// once vmcnt has drained (the fused launch hands these rows to other XCDs).
+template <int BM, int MI, int NI, bool PARTIAL, bool COHERENT>
 __device__ __forceinline__ void epilogue_linear1(const v4f (&acc)[MI][NI], const GemmArgs& g, int m0, int rows,
                                                  int wrow0, int gcol0, const float* row_w, const int* row_tok,
                                                  int lane) {
@@ -413,11 +447,18 @@ __device__ __forceinline__ void epilogue_linear1(const v4f (&acc)[MI][NI], const
                 // 32-bit offsets from uniform bases (cap * I < 2^31 is checked on the host)
                 if (!PARTIAL || row_local < rows) {
                     const uint32_t row = (uint32_t)(m0 + row_local);
-                    *reinterpret_cast<int*>(g.out_q + (row * (uint32_t)n_q + (uint32_t)(gcol / 2 + 4 * j8))) = q;
+                    int* qp = reinterpret_cast<int*>(g.out_q + (row * (uint32_t)n_q + (uint32_t)(gcol / 2 + 4 * j8)));
                     // Linear2 K-step = 256-column block of Z, byte = 64-column group within it
-                    if (j8 == 0)
-                        g.out_sf[tile_scale_offset<BM, PARTIAL>(m0, row_local, ksteps2, gcol / kTileN, g.bm_shift) +
-                                 (uint32_t)((gcol % kTileN) / 64)] = (uint8_t)code;
+                    uint8_t* sp = g.out_sf + tile_scale_offset<BM, PARTIAL>(m0, row_local, ksteps2, gcol / kTileN,
+                                                                            g.bm_shift) +
+                                  (uint32_t)((gcol % kTileN) / 64);
+                    if constexpr (COHERENT) {
+                        __hip_atomic_store(qp, q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (j8 == 0) __hip_atomic_store(sp, (uint8_t)code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    } else {
+                        *qp = q;
+                        if (j8 == 0) *sp = (uint8_t)code;
+                    }
                 }
             }
         }
@@ -447,10 +488,11 @@ __device__ __forceinline__ void epilogue_linear2(const v4f (&acc)[MI][NI], const
         }
 }
 
-template <int BM, int MI, int NI, bool L1, bool PARTIAL>
+template <int BM, int MI, int NI, bool L1, bool PARTIAL, bool COHERENT = false>
 __device__ __forceinline__ void epilogue(const v4f (&acc)[MI][NI], const GemmArgs& g, const TileId& t, int wrow0,
                                          int gcol0, const float* row_w, const int* row_tok, int lane) {
-    if constexpr (L1) epilogue_linear1<BM, MI, NI, PARTIAL>(acc, g, t.m, t.rows, wrow0, gcol0, row_w, row_tok, lane);
+    if constexpr (L1)
+        epilogue_linear1<BM, MI, NI, PARTIAL, COHERENT>(acc, g, t.m, t.rows, wrow0, gcol0, row_w, row_tok, lane);
     else epilogue_linear2<BM, MI, NI, PARTIAL>(acc, g, t.m, t.rows, wrow0, gcol0, row_tok, lane);
 }
 
@@ -492,14 +534,14 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
     __shared__ int row_tok[BM];
 
     TileId t;
-    if (!tile_of_block(g, t)) return;
+    if (!tile_of_block(g, 256, t)) return;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int KT = g.K / kBK;
     load_row_tables<BM, L1>(g, t, row_w, row_tok, tid);
 
     StageDma<BM, 256, C::A_PW, C::B_PW, C::SB_PW> dma;
-    dma.init_a(g, t.m, t.rows, row_tok, L1, w, 4, lane);
+    dma.init_a(g, t.m, t.rows, row_tok, L1, w, 4);
     dma.init_b(g, t, w, 4);
     auto issue = [&](int kt) {
         uint8_t* st = smem + (kt % L::NS) * L::STAGE;
@@ -559,7 +601,24 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
 // rows are fetched, the rows by the time the tile's first stage is issued,
 // the weights by the time the tile's multiplication starts.  Below that the
 // kernel runs one tile per workgroup.
-template <int BM, bool L1>
+//
+// Fused launch (Linear1 and Linear2 in one kernel: the single-launch
+// schedule of the reading notes, where Linear2 blocks wait on arrival marks
+// set by the Linear1 epilogue).  Each workgroup runs the loop above over its
+// Linear1 tiles, then again, after a barrier, over its Linear2 tiles.  When
+// both groups have stored the h rows of a Linear1 tile (each wave fencing
+// its stores at device scope), one lane stores the launch's epoch into that
+// tile's flag.  In the Linear2 run group 1 also loads the flags of tile
+// ci + 1's M-tile with its row tables (gate[.. % 3], read device-coherent),
+// and before it issues a tile's first stage it checks that all of them hold
+// the epoch, else sleeps and loads them again.  A workgroup's own Linear1
+// tiles are all flagged before its Linear2 run starts, every workgroup runs
+// its Linear1 tiles first, and the grid is at most one workgroup per CU, all
+// resident: every awaited tile is being computed.  A Linear2 tile reads only
+// rows whose Linear1 tiles are done and no XCD reads those lines earlier in
+// the launch, so plain loads see the stored values.  After kGateSpins polls
+// the wait gives up and sets the status word instead of hanging.
+template <int BM, bool L1, bool FUSED>
 struct CfgPP {
     using L = StageLayout<BM, 512>;
     static constexpr bool SPLIT_ROWS = BM == 128;  // the groups split the rows, else the columns
@@ -570,59 +629,90 @@ struct CfgPP {
     static constexpr int SB_PW = L::SB_INSTR / 4;
     static constexpr int D0 = B_PW + SB_PW + 1;
     static constexpr int A_PW = L::A_INSTR >= 4 ? L::A_INSTR / 4 : 1;  // group 1: rows, scales, + row tables
-    static constexpr int D1 = A_PW + 1 + 1;  // + 1 on the first stage of each tile (Linear1)
+    static constexpr bool GATED = FUSED && !L1;  // + the Linear1 flags of the next tile
+    static constexpr int D1 = A_PW + 1 + 1 + (GATED ? 1 : 0);  // + 1 on the first stage of each tile (Linear1)
     static constexpr int MIN_KT_PERSISTENT = 2 * (L::NS - 1);
-    static_assert(2 * D0 < kNoVmWait && 2 * D1 < kNoVmWait, "vmcnt range");
+    static_assert(2 * D0 < kNoVmWait && 2 * D1 + 1 < kNoVmWait, "vmcnt range");
     static_assert(BM <= 128, "row tables hold 128 rows");
 };
 constexpr int kTableSlots = 3;
+constexpr int kGateSpins = 1 << 18;  // flag polls (a few us each) before a Linear2 tile gives up
 
-template <int BM, bool L1, bool PARTIAL>
-__global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
-    using C = CfgPP<BM, L1>;
+// Completion flags of a fused launch.
+struct FusedSync {
+    uint32_t* flags;   // one word per Linear1 tile, [M-tile][Linear1 N-tile]
+    uint32_t* status;  // set to 1 if a Linear2 tile stopped waiting
+    uint32_t epoch;    // value of a set flag in this launch
+    int nt1;           // Linear1 N-tiles
+};
+
+// LDS of the persistent kernels.
+template <int BM>
+struct PPShared {
+    __attribute__((aligned(1024))) uint8_t smem[StageLayout<BM, 512>::NS * StageLayout<BM, 512>::STAGE];
+    int desc[kTableSlots][64];       // words 0-3: the tile's list entry
+    int meta[kTableSlots][256];      // [0, 128): row tokens; [128, 256): top-k slots
+    float wts[kTableSlots][128];     // Linear1: top-k weights of the rows
+    uint32_t gate[kTableSlots][64];  // fused Linear2: the Linear1 flags of the tile's M-tile
+};
+
+// The tiles of one persistent run, in order: j < n_a: first_a + j * stride_a,
+// then first_b + (j - n_a) * stride_b.
+struct TileSeq {
+    int first_a, n_a, stride_a, first_b, stride_b, n;
+    __device__ __forceinline__ int index(int j) const {
+        return j < n_a ? first_a + j * stride_a : first_b + (j - n_a) * stride_b;
+    }
+};
+
+// One persistent run over the tiles `seq` of g's list.
+template <int BM, bool L1, bool PARTIAL, bool FUSED>
+__device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync, const TileSeq& seq,
+                                       PPShared<BM>& sh) {
+    const int ntiles = seq.n;
+    using C = CfgPP<BM, L1, FUSED>;
     using L = typename C::L;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[L::NS * L::STAGE];
-    __shared__ int desc[kTableSlots][64];   // words 0-3: the tile's list entry
-    __shared__ int meta[kTableSlots][256];  // [0, 128): row tokens; [128, 256): top-k slots
-    __shared__ float wts[kTableSlots][128]; // Linear1: top-k weights of the rows
-
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int grp = w >> 2, wq = w & 3;
     const int KT = g.K / kBK;
-
-    // ---- this workgroup's tiles
-    const int total = g.scalars[g.count_idx];
-    const int share = (total + kNumXcd - 1) / kNumXcd;
-    const int nslots = gridDim.x / kNumXcd;
-    const int xcd = blockIdx.x % kNumXcd;
-    const int first = xcd * share + blockIdx.x / kNumXcd;
-    const int end = min((xcd + 1) * share, total);
-    if (first >= end) return;
-    const int ntiles = (end - first + nslots - 1) / nslots;
     const int S = ntiles * KT;
-    auto tile_entry = [&](int j) { return g.tiles + kTileWords * (first + min(j, ntiles - 1) * nslots); };
+    auto tile_entry = [&](int j) {
+        return static_cast<const int32_t*>(uniform_ptr(g.tiles + kTileWords * seq.index(min(j, ntiles - 1))));
+    };
 
     // ---- table loads (one DMA instruction per wave)
     auto load_desc = [&](int j) {  // group 0
         j = min(j, ntiles - 1);
-        dma4((uint32_t)min(lane, kTileWords - 1) * 4, tile_entry(j), lds_addr(&desc[j % kTableSlots][0]));
+        dma4((uint32_t)min(fresh_lane(), kTileWords - 1) * 4, tile_entry(j), lds_addr(&sh.desc[j % kTableSlots][0]));
+    };
+    // fused Linear2: the Linear1 flags of tile t's M-tile, read device-coherent (sc1: other
+    // workgroups, possibly on other XCDs, store them)
+    auto load_flags = [&](int j, const TileId& t) {
+        asm volatile("global_load_lds_dword %0, %1 sc1"
+                     ::"v"((uint32_t)(t.mt * sync.nt1 + min(fresh_lane(), sync.nt1 - 1)) * 4u), "s"(sync.flags),
+                       "{m0}"(lds_addr(&sh.gate[j % kTableSlots][0]))
+                     : "memory");
     };
     // rows past the tile's valid count load whatever the tables hold there (the
     // tables reserve slack rows past the last block); every reader masks them
-    auto load_meta = [&](int j, int m) {  // group 1; m = first row of tile j
+    auto load_meta = [&](int j, const TileId& t) {  // group 1; t = tile j
         j = min(j, ntiles - 1);
         const int part = wq >> 1, half = wq & 1;
-        const int row = min(half * 64 + lane, BM - 1);
-        const int32_t* src = (part == 1 ? g.row_topk : g.row_token) + m;
-        dma4((uint32_t)row * 4, src, lds_addr(&meta[j % kTableSlots][part * 128 + half * 64]));
+        const int row = min(half * 64 + fresh_lane(), BM - 1);
+        const int32_t* src = (part == 1 ? g.row_topk : g.row_token) + t.m;
+        dma4((uint32_t)row * 4, src, lds_addr(&sh.meta[j % kTableSlots][part * 128 + half * 64]));
+        if constexpr (C::GATED) load_flags(j, t);
     };
     auto read_entry = [&](int j, TileId& t) {
         j = min(j, ntiles - 1);
-        const int a = __builtin_amdgcn_readfirstlane(desc[j % kTableSlots][0]);
-        const int b = __builtin_amdgcn_readfirstlane(desc[j % kTableSlots][1]);
-        const int r = __builtin_amdgcn_readfirstlane(desc[j % kTableSlots][2]);
-        t.m = a; t.n = b >> 16; t.e = b & 0xFFFF; t.rows = r;
+        const int* d = sh.desc[j % kTableSlots];
+        t.m = __builtin_amdgcn_readfirstlane(d[0]);
+        const int b = __builtin_amdgcn_readfirstlane(d[1]);
+        t.n = b >> 16;
+        t.e = b & 0xFFFF;
+        t.rows = PARTIAL ? __builtin_amdgcn_readfirstlane(d[2]) : BM;
+        t.mt = FUSED ? __builtin_amdgcn_readfirstlane(d[3]) : 0;
     };
 
     const int wrow0 = C::SPLIT_ROWS ? grp * C::WTM : 0;
@@ -635,7 +725,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
     wait_and_barrier<0>();
     TileId t0;
     read_entry(0, t0);
-    if (grp == 1) load_meta(0, t0.m);
+    if (grp == 1) load_meta(0, t0);
     wait_and_barrier<0>();
 
     if (grp == 0) {
@@ -648,7 +738,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
                 read_entry(s / KT, t);
                 dma.init_b(g, t, wq, 4);
             }
-            dma.issue_b(smem + (s % L::NS) * L::STAGE, s % KT, lane);
+            dma.issue_b(sh.smem + (s % L::NS) * L::STAGE, s % KT, lane);
             load_desc(max(s - (L::NS - 1), 0) / KT + 2);
         };
 #pragma unroll
@@ -662,7 +752,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
             // of its A fragments here and the second half at the start of its MFMA phase (stage gs is
             // still intact then: it is refilled only after B_2gs+2)
             constexpr int MH = C::MI / 2;
-            const uint8_t* st = smem + (gs % L::NS) * L::STAGE;
+            const uint8_t* st = sh.smem + (gs % L::NS) * L::STAGE;
             Frags<C::MI, C::NI> f;
             read_frags<BM, 512, C::MI, C::NI, 0, MH>(f, st, wrow0, wcol0, lane);
             wait_and_barrier<kNoVmWait>();                                 // B_2gs+1
@@ -670,21 +760,45 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
             mfma_step<C::MI, C::NI, 0, MH>(acc, f, kt == 0);
             mfma_step<C::MI, C::NI, MH, C::MI>(acc, f, kt == 0);
             if (++kt == KT) {
-                epilogue<BM, C::MI, C::NI, L1, PARTIAL>(acc, g, ct, wrow0, ct.n * 512 + wcol0, wts[ci % kTableSlots],
-                                               meta[ci % kTableSlots], lane);
+                epilogue<BM, C::MI, C::NI, L1, PARTIAL, FUSED>(acc, g, ct, wrow0, ct.n * 512 + wcol0,
+                                                               sh.wts[ci % kTableSlots], sh.meta[ci % kTableSlots],
+                                                               lane);
+                if constexpr (FUSED && L1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // stores complete
                 kt = 0;
                 ++ci;
             }
         }
+        if constexpr (FUSED) __syncthreads();  // B_2S
     } else {
         StageDma<BM, 512, C::A_PW, 1, 1> dma;
-        dma.init_a(g, t0.m, t0.rows, meta[0], L1, wq, 4, lane);
+        // fused Linear2: wait until every Linear1 tile of t's M-tile is done.  The flags came with
+        // the row tables; while one is not set yet, sleep and load them again (the wait for that load
+        // drains this wave's DMA queue, which only makes the later vmcnt waits conservative)
+        auto gate_open = [&](int j, const TileId& t) {
+            if constexpr (C::GATED) {
+                const uint32_t* fl = sh.gate[j % kTableSlots];
+                for (int it = 0;; ++it) {
+                    const int l = fresh_lane();
+                    const bool ok = l >= sync.nt1 || fl[l] == sync.epoch;
+                    if (__builtin_amdgcn_ballot_w64(!ok) == 0) return;
+                    if (it == kGateSpins) {
+                        if (l == 0) __hip_atomic_store(sync.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        return;
+                    }
+                    __builtin_amdgcn_s_sleep(16);
+                    load_flags(j, t);
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
+            }
+        };
+        gate_open(0, t0);
+        dma.init_a(g, t0.m, t0.rows, sh.meta[0], L1, wq, 4);
         TileId tn;  // tile whose rows the table load fetches
         read_entry(1, tn);
         // Linear1: byte offset into topk_w of this lane's row of the issued tile
-        const int w_row = min((wq & 1) * 64 + lane, BM - 1);
         auto weight_offset = [&](int j, int rows) {
-            const int* mt = meta[j % kTableSlots];
+            const int w_row = min((wq & 1) * 64 + fresh_lane(), BM - 1);
+            const int* mt = sh.meta[j % kTableSlots];
             const int t = w_row < rows ? mt[w_row] : -1;
             return t >= 0 ? (uint32_t)(t * g.topk + mt[128 + w_row]) * 4u : 0u;
         };
@@ -693,41 +807,118 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
             if (s % KT == 0 && s > 0) {
                 TileId t;
                 read_entry(s / KT, t);
-                dma.init_a(g, t.m, t.rows, meta[(s / KT) % kTableSlots], L1, wq, 4, lane);
+                gate_open(s / KT, t);
+                dma.init_a(g, t.m, t.rows, sh.meta[(s / KT) % kTableSlots], L1, wq, 4);
                 if (L1) w_off = weight_offset(s / KT, t.rows);
             }
-            dma.issue_a(smem + (s % L::NS) * L::STAGE, s % KT, lane);
-            load_meta(max(s - (L::NS - 1), 0) / KT + 1, tn.m);
-            if (L1 && s % KT == 0) dma4(w_off, g.topk_w, lds_addr(&wts[(s / KT) % kTableSlots][(wq & 1) * 64]));
+            dma.issue_a(sh.smem + (s % L::NS) * L::STAGE, s % KT, lane);
+            load_meta(max(s - (L::NS - 1), 0) / KT + 1, tn);
+            if (L1 && s % KT == 0)
+                dma4(w_off, g.topk_w, lds_addr(&sh.wts[(s / KT) % kTableSlots][(wq & 1) * 64]));
         };
         // does a stage in (s, s + n] start a tile (and so carry the weight gather)?
         auto starts_tile = [&](int s, int n) { return L1 && n > 0 && ((s % KT) + n >= KT) ? 1 : 0; };
+        // fused Linear1: the flag of a finished tile is stored after the next barrier, when both
+        // groups' stores of that tile are fenced
+        bool signal = false;
+        TileId done;
+        auto store_flag = [&]() {
+            if (signal && w == 4 && lane == 0)
+                __hip_atomic_store(sync.flags + done.mt * sync.nt1 + done.n, sync.epoch, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            signal = false;
+        };
 #pragma unroll
         for (int s = 0; s < L::NS - 1; ++s)
             if (s < S) issue(s);
         wait_stages_and_barrier<C::D1>(min(L::NS - 2, S - 1), starts_tile(0, min(L::NS - 2, S - 1)));  // B_0
         for (int gs = 0, kt = 0, ci = 0; gs < S; ++gs) {
             wait_and_barrier<kNoVmWait>();                                 // B_2gs+1
+            if constexpr (FUSED && L1) store_flag();
             if (kt == 0) {
                 read_entry(ci, ct);
                 read_entry(ci + 1, tn);
             }
             if (gs + L::NS - 1 < S) issue(gs + L::NS - 1);
             Frags<C::MI, C::NI> f;
-            read_frags<BM, 512>(f, smem + (gs % L::NS) * L::STAGE, wrow0, wcol0, lane);
+            read_frags<BM, 512>(f, sh.smem + (gs % L::NS) * L::STAGE, wrow0, wcol0, lane);
             if (gs + 1 < S) {  // B_2gs+2
                 const int n = min(L::NS - 2, S - 2 - gs);
                 wait_stages_and_barrier<C::D1>(n, starts_tile(gs + 1, n));
             }
             mfma_step(acc, f, kt == 0);
             if (++kt == KT) {
-                epilogue<BM, C::MI, C::NI, L1, PARTIAL>(acc, g, ct, wrow0, ct.n * 512 + wcol0, wts[ci % kTableSlots],
-                                               meta[ci % kTableSlots], lane);
+                epilogue<BM, C::MI, C::NI, L1, PARTIAL, FUSED>(acc, g, ct, wrow0, ct.n * 512 + wcol0,
+                                                               sh.wts[ci % kTableSlots], sh.meta[ci % kTableSlots],
+                                                               lane);
+                if constexpr (FUSED && L1) {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // stores complete
+                    signal = true;
+                    done = ct;
+                }
                 kt = 0;
                 ++ci;
             }
         }
+        if constexpr (FUSED) {
+            __syncthreads();  // B_2S
+            if constexpr (L1) store_flag();
+        }
     }
+}
+
+// Round-robin share of an XCD's list range [begin, end): tiles begin + slot + j * nslots.
+__device__ __forceinline__ TileSeq round_robin(int begin, int end, int slot, int nslots) {
+    const int first = begin + slot;
+    const int n = first < end ? (end - first + nslots - 1) / nslots : 0;
+    return TileSeq{first, n, nslots, 0, 1, n};
+}
+
+template <int BM, bool L1, bool PARTIAL>
+__global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
+    __shared__ PPShared<BM> sh;
+    int begin, end;
+    xcd_chunk(g, g.N / 512, blockIdx.x % kNumXcd, begin, end);
+    const TileSeq seq = round_robin(begin, end, blockIdx.x / kNumXcd, gridDim.x / kNumXcd);
+    if (seq.n == 0) return;
+    pp_run<BM, L1, PARTIAL, false>(g, FusedSync{}, seq, sh);
+}
+
+struct FusedArgs {
+    GemmArgs g1, g2;  // Linear1, Linear2
+    FusedSync sync;
+};
+
+// Linear1 then Linear2 in one launch.  Each XCD runs the Linear1 and then the Linear2 tiles of its
+// M-tiles.  Its Linear1 tiles go round-robin to its workgroups, so the first r1 slots run one tile
+// more than the others ("light" workgroups, L of them).  While the others finish that tile, the
+// light workgroups run the first L * d Linear2 tiles (d = Linear2 tiles per Linear1 tile of time,
+// from the K-steps; the list runs M-tile by M-tile, so these need the M-tiles the first Linear1
+// round computed); the rest go round-robin to all workgroups.
+template <int BM, bool PARTIAL>
+__global__ __launch_bounds__(512, 1) void gemm_fused_kernel(FusedArgs fa) {
+    __shared__ PPShared<BM> sh;
+    const int nslots = gridDim.x / kNumXcd, xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+    int b1, e1, b2, e2;
+    xcd_chunk(fa.g1, fa.g1.N / 512, xcd, b1, e1);
+    xcd_chunk(fa.g2, fa.g2.N / 512, xcd, b2, e2);
+    const TileSeq s1 = round_robin(b1, e1, slot, nslots);
+    if (s1.n > 0) pp_run<BM, true, PARTIAL, true>(fa.g1, fa.sync, s1, sh);
+    wait_and_barrier<0>();  // the Linear1 run's table loads have landed before the tables are reused
+
+    const int r1 = (e1 - b1) % nslots, nl = r1 > 0 ? nslots - r1 : 0;  // light workgroups: slots >= r1
+    const int c1 = fa.g1.K / kBK + 1, c2 = fa.g2.K / kBK + 1;            // tile costs in K-steps
+    const int d = (2 * c1 + c2) / (2 * c2);
+    const int na_all = min(nl * d, e2 - b2);
+    TileSeq s2;
+    const int li = slot - r1;
+    s2.first_a = b2 + li;
+    s2.stride_a = max(nl, 1);
+    s2.n_a = (r1 > 0 && li >= 0 && li < na_all) ? (na_all - li + nl - 1) / nl : 0;
+    s2.first_b = b2 + na_all + slot;
+    s2.stride_b = nslots;
+    s2.n = s2.n_a + (s2.first_b < e2 ? (e2 - s2.first_b + nslots - 1) / nslots : 0);
+    if (s2.n > 0) pp_run<BM, false, PARTIAL, true>(fa.g2, fa.sync, s2, sh);
 }
 
 // Compute units of the current device (cached per device).
@@ -743,15 +934,25 @@ int cu_count() {
     return c;
 }
 
+// K-steps a tile needs for the persistent ping-pong kernel with M-tile bmg.
+int min_kt_persistent(int bmg) {
+    switch (bmg) {
+        case 16: return CfgPP<16, true, false>::MIN_KT_PERSISTENT;
+        case 128: return CfgPP<128, true, false>::MIN_KT_PERSISTENT;
+        default: return 1 << 30;
+    }
+}
+
+int64_t persistent_grid(int64_t all) {
+    const int64_t cus = cu_count() / kNumXcd * kNumXcd;  // one workgroup per CU
+    return std::max<int64_t>(kNumXcd, std::min(all, cus));
+}
+
+// all: workgroups for one tile each
 template <int BM, bool L1, bool PARTIAL>
-hipError_t launch_bm(const GemmArgs& args, int64_t tiles, hipStream_t stream) {
-    const int64_t all = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;  // one workgroup per tile
+hipError_t launch_bm(const GemmArgs& args, int64_t all, hipStream_t stream) {
     if (gemm_bn(args.N) == 512) {
-        int64_t grid = all;
-        if (args.K / kBK >= CfgPP<BM, L1>::MIN_KT_PERSISTENT) {  // persistent: one workgroup per CU
-            const int64_t cus = cu_count() / kNumXcd * kNumXcd;
-            grid = std::max<int64_t>(kNumXcd, std::min(all, cus));
-        }
+        const int64_t grid = args.K / kBK >= min_kt_persistent(BM) ? persistent_grid(all) : all;
         hipLaunchKernelGGL((gemm_pp_kernel<BM, L1, PARTIAL>), dim3(grid), dim3(512), 0, stream, args);
     } else {
         hipLaunchKernelGGL((gemm4_kernel<BM, L1, PARTIAL>), dim3(all), dim3(256), 0, stream, args);
@@ -759,15 +960,21 @@ hipError_t launch_bm(const GemmArgs& args, int64_t tiles, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Workgroups for one tile each of a GEMM with N columns: every XCD gets the slots of ceil(M-tiles / 8)
+// M-tiles (xcd_chunk), for an upper bound on the M-tiles (the padded rows are not known on the host:
+// every M-tile but each expert's last covers bmg / bm whole blocks).
+int64_t one_tile_grid(const GemmProblem& p, int N) {
+    const int bm = p.shape->block_m, bmg = gemm_bm(bm);
+    const int64_t blocks = p.cap / bm;
+    const int64_t mtiles = std::min<int64_t>(blocks, blocks / (bmg / bm) + p.shape->num_experts);
+    return kNumXcd * ((mtiles + kNumXcd - 1) / kNumXcd) * (N / gemm_bn(N));
+}
+
 template <bool L1>
 hipError_t launch_gemm(const GemmProblem& p, GemmArgs args, hipStream_t stream) {
     const int bm = p.shape->block_m, bmg = gemm_bm(bm);
     args.bm_shift = 31 - __builtin_clz((unsigned)bm);
-    // upper bound on the M-tiles (the padded rows are not known yet): every M-tile but each expert's
-    // last covers bmg / bm whole blocks
-    const int64_t blocks = p.cap / bm;
-    const int64_t mtiles = std::min<int64_t>(blocks, blocks / (bmg / bm) + p.shape->num_experts);
-    const int64_t tiles = mtiles * (args.N / gemm_bn(args.N));
+    const int64_t tiles = one_tile_grid(p, args.N);
     if (tiles == 0) return hipSuccess;
     if (bmg == bm) {
         switch (bmg) {
@@ -788,13 +995,12 @@ GemmArgs common_args(const GemmProblem& p) {
     a.row_token = p.plan->row_token;
     a.row_topk = p.plan->row_topk;
     a.topk = p.shape->topk;
+    a.bm_shift = 31 - __builtin_clz((unsigned)p.shape->block_m);
     return a;
 }
 
-}  // namespace
-
-hipError_t launch_linear1(const GemmProblem& p, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
-                          const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf, hipStream_t stream) {
+GemmArgs linear1_args(const GemmProblem& p, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
+                      const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf) {
     GemmArgs a = common_args(p);
     a.tiles = p.plan->tiles1;
     a.count_idx = 4;
@@ -802,18 +1008,75 @@ hipError_t launch_linear1(const GemmProblem& p, const uint8_t* x, const uint8_t*
     a.a = x; a.a_sf = x_sf; a.b = w1; a.b_sf = w1_sf;
     a.out_q = h_q; a.out_sf = h_sf; a.out_bf16 = nullptr;
     a.K = p.shape->hidden; a.N = 2 * p.shape->intermediate;
-    return launch_gemm<true>(p, a, stream);
+    return a;
 }
 
-hipError_t launch_linear2(const GemmProblem& p, const uint8_t* h_q, const uint8_t* h_sf, const uint8_t* w2,
-                          const uint8_t* w2_sf, uint16_t* yslot, hipStream_t stream) {
+GemmArgs linear2_args(const GemmProblem& p, const uint8_t* h_q, const uint8_t* h_sf, const uint8_t* w2,
+                      const uint8_t* w2_sf, uint16_t* yslot) {
     GemmArgs a = common_args(p);
     a.tiles = p.plan->tiles2;
     a.count_idx = 5;
     a.a = h_q; a.a_sf = h_sf; a.b = w2; a.b_sf = w2_sf;
     a.out_q = nullptr; a.out_sf = nullptr; a.out_bf16 = yslot;
     a.K = p.shape->intermediate; a.N = p.shape->hidden;
-    return launch_gemm<false>(p, a, stream);
+    return a;
+}
+
+// Epoch of a fused launch: a fresh value per launch, never 0, from a random start so that flag words
+// left in a workspace by an earlier process or launch do not match.
+uint32_t next_epoch() {
+    static std::atomic<uint32_t> counter{[] {
+        std::random_device rd;
+        return (uint32_t)rd();
+    }()};
+    uint32_t e;
+    do e = counter.fetch_add(1, std::memory_order_relaxed); while (e == 0);
+    return e;
+}
+
+}  // namespace
+
+bool fused_supported(const moe_shape& s) {
+    const int bmg = gemm_bm(s.block_m);
+    const int N1 = 2 * s.intermediate, N2 = s.hidden;
+    return gemm_bn(N1) == 512 && gemm_bn(N2) == 512 && N1 / 512 <= 64 &&
+           s.hidden / kBK >= min_kt_persistent(bmg) && s.intermediate / kBK >= min_kt_persistent(bmg);
+}
+
+hipError_t launch_expert_ffn(const GemmProblem& p, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
+                             const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf,
+                             const uint8_t* w2, const uint8_t* w2_sf, uint16_t* yslot, uint32_t* flags,
+                             uint32_t* status, hipStream_t stream) {
+    FusedArgs fa{};
+    fa.g1 = linear1_args(p, x, x_sf, topk_w, w1, w1_sf, h_q, h_sf);
+    fa.g2 = linear2_args(p, h_q, h_sf, w2, w2_sf, yslot);
+    if (!fused_supported(*p.shape)) {
+        hipError_t e = launch_gemm<true>(p, fa.g1, stream);
+        if (e != hipSuccess) return e;
+        return launch_gemm<false>(p, fa.g2, stream);
+    }
+    fa.sync.flags = flags;
+    fa.sync.status = status;
+    fa.sync.epoch = next_epoch();
+    fa.sync.nt1 = fa.g1.N / 512;
+    const int64_t tiles = std::max(one_tile_grid(p, fa.g1.N), one_tile_grid(p, fa.g2.N));
+    if (tiles == 0) return hipSuccess;
+    const dim3 grid((unsigned)persistent_grid(tiles)), block(512);
+    const int bm = p.shape->block_m, bmg = gemm_bm(bm);
+    if (bmg == 16) hipLaunchKernelGGL((gemm_fused_kernel<16, false>), grid, block, 0, stream, fa);
+    else if (bm == 128) hipLaunchKernelGGL((gemm_fused_kernel<128, false>), grid, block, 0, stream, fa);
+    else hipLaunchKernelGGL((gemm_fused_kernel<128, true>), grid, block, 0, stream, fa);
+    return hipGetLastError();
+}
+
+hipError_t launch_linear1(const GemmProblem& p, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
+                          const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf, hipStream_t stream) {
+    return launch_gemm<true>(p, linear1_args(p, x, x_sf, topk_w, w1, w1_sf, h_q, h_sf), stream);
+}
+
+hipError_t launch_linear2(const GemmProblem& p, const uint8_t* h_q, const uint8_t* h_sf, const uint8_t* w2,
+                          const uint8_t* w2_sf, uint16_t* yslot, hipStream_t stream) {
+    return launch_gemm<false>(p, linear2_args(p, h_q, h_sf, w2, w2_sf, yslot), stream);
 }
 
 }  // namespace moe

@@ -30,7 +30,9 @@ inline int gemm_bm(int block_m) { return block_m >= 32 ? 128 : block_m; }
 // Rows past `cap` that the row tables reserve, so a 128-row tile starting at the last block reads
 // allocated memory (the GEMMs mask every row past the tile's valid count).
 constexpr int kRowSlack = 128;
-// Words per tile-list entry: {first row, n << 16 | e, valid rows, 0}.
+// Words per tile-list entry: {first row, n << 16 | e, valid rows, M-tile index}; M-tiles are
+// numbered expert by expert over both lists, so Linear1 tile (M-tile i, N-tile n) and the Linear2
+// tiles of M-tile i can find each other.
 constexpr int kTileWords = 4;
 
 struct PlanLayout {
@@ -80,7 +82,7 @@ inline PlanLayout plan_layout(const moe_shape& s) {
 // Offsets (bytes) inside a forward workspace: the plan region first.
 struct ForwardLayout {
     PlanLayout plan;
-    size_t plan_base = 0, h_q = 0, h_sf = 0, yslot = 0, total = 0;
+    size_t plan_base = 0, h_q = 0, h_sf = 0, yslot = 0, flags = 0, status = 0, total = 0;
 };
 
 inline ForwardLayout forward_layout(const moe_shape& s) {
@@ -92,6 +94,8 @@ inline ForwardLayout forward_layout(const moe_shape& s) {
     F.h_q = take((size_t)F.plan.cap * s.intermediate);
     F.h_sf = take((size_t)F.plan.cap * (s.intermediate / 32));
     F.yslot = take((size_t)F.plan.cap * s.hidden * 2);
+    F.flags = take((size_t)F.plan.max_tiles1 * 4);  // one word per Linear1 tile (fused launch)
+    F.status = take(4);
     F.total = o;
     return F;
 }
@@ -121,13 +125,21 @@ struct GemmProblem {
 };
 // Linear1 gathers its A rows and their scales (x [T, H], x_sf [T, H/32]) and
 // the top-k weights through the plan's row tables; Linear2 reads h_q and h_sf
-// (per-row-block layout [cap/BM][I/128][BM][4]) as the Linear1 epilogue wrote
+// (per-block layout [cap/bm][I/128][bm][4]) as the Linear1 epilogue wrote
 // them.  w*, w*_sf: weights in the tiled layout of moe_prepare.hip.
 hipError_t launch_linear1(const GemmProblem& g, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
                           const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf,
                           hipStream_t stream);
 hipError_t launch_linear2(const GemmProblem& g, const uint8_t* h_q, const uint8_t* h_sf, const uint8_t* w2,
                           const uint8_t* w2_sf, uint16_t* yslot, hipStream_t stream);
+// Both GEMMs in one persistent launch when the shape allows it (fused_supported), else the two
+// launches above.  flags: one word per Linear1 tile, any initial contents; status: set to 1 if a
+// Linear2 tile stopped waiting for its rows (never cleared here).
+bool fused_supported(const moe_shape& s);
+hipError_t launch_expert_ffn(const GemmProblem& g, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
+                             const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf,
+                             const uint8_t* w2, const uint8_t* w2_sf, uint16_t* yslot, uint32_t* flags,
+                             uint32_t* status, hipStream_t stream);
 hipError_t launch_tile_weights(int which, int N, int K, int E, const uint8_t* w, const uint8_t* w_sf,
                                uint8_t* w_out, uint8_t* sf_out, hipStream_t stream);
 hipError_t launch_combine(const moe_shape& s, const uint16_t* yslot, const int32_t* slot, uint16_t* y,

@@ -75,9 +75,9 @@ __device__ int block_inclusive_scan(int v, int* scratch) {
 
 // GEMM tile lists from the padded offsets soff (LDS, E+1).  An M-tile covers up to bmg rows (bmg / bm
 // blocks) of one expert; expert e has ceil(blocks_e / (bmg / bm)) M-tiles, whose exclusive prefix over
-// experts goes to tb (LDS scratch, E+1).  For a GEMM with nt N-tiles, expert e's tiles start at
-// tb[e] * nt and run N-tile by N-tile over all of e's M-tiles; entry l = {first row, n << 16 | e,
-// valid rows, 0}.  Called by every thread of the workgroup; workgroup `part` of `parts` writes the
+// experts goes to tb (LDS scratch, E+1), so M-tiles are numbered expert by expert.  For a GEMM with nt
+// N-tiles the list runs M-tile by M-tile, all N-tiles of each: entry l = mt * nt + n = {first row,
+// n << 16 | e, valid rows, mt}.  A range of M-tiles is then a contiguous range of both GEMMs' lists.  Called by every thread of the workgroup; workgroup `part` of `parts` writes the
 // entries l with l / blockDim.x = part mod parts.  scalars[4], [5] = tiles of each GEMM (if `counts`).
 __device__ void write_tile_lists(const int32_t* soff, int E, int bm, int32_t* tb, const PlanPtrs& p, int part,
                                  int parts, bool counts) {
@@ -113,19 +113,18 @@ __device__ void write_tile_lists(const int32_t* soff, int E, int bm, int32_t* tb
         int32_t* tiles = pass == 0 ? p.tiles1 : p.tiles2;
         const int total = mt_total * nt;
         for (int l = part * blockDim.x + threadIdx.x; l < total; l += parts * blockDim.x) {
-            int lo = 0, hi = E - 1;  // largest e whose first tile is <= l (that expert has rows)
+            const int mt = l / nt, n = l - mt * nt;
+            int lo = 0, hi = E - 1;  // the expert of M-tile mt: largest e with tb[e] <= mt
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
-                if (tb[mid] * nt <= l) lo = mid; else hi = mid - 1;
+                if (tb[mid] <= mt) lo = mid; else hi = mid - 1;
             }
-            const int me = tb[lo + 1] - tb[lo];
-            const int local = l - tb[lo] * nt;
-            const int m0 = soff[lo] + (local % me) * bmg;
+            const int m0 = soff[lo] + (mt - tb[lo]) * bmg;
             int32_t* t = tiles + (size_t)kTileWords * l;
             t[0] = m0;
-            t[1] = ((local / me) << 16) | lo;
+            t[1] = (n << 16) | lo;
             t[2] = min(bmg, soff[lo + 1] - m0);
-            t[3] = 0;
+            t[3] = mt;
         }
     }
 }
