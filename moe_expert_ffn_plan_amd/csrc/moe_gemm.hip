@@ -318,13 +318,19 @@ struct StageDma {
         }
         dma4(sa_off, a_sf + (size_t)kt * sa_kt, lds_addr(st + L::A_BYTES + L::B_BYTES + sa_blk * 256));
     }
-    __device__ __forceinline__ void issue_b(uint8_t* st, int kt, int lane) const {
+    // weight blocks OFF + i * bnw + bw, i < NB (1 KiB each, 16 per 256 columns)
+    template <int NB, int OFF>
+    __device__ __forceinline__ void issue_b_blocks(uint8_t* st, int kt, int lane) const {
 #pragma unroll
-        for (int i = 0; i < B_PW; ++i) {
-            const int blk = i * bnw + bw;  // 1 KiB block of this stage's B (16 per 256 columns)
+        for (int i = 0; i < NB; ++i) {
+            const int blk = OFF + i * bnw + bw;
             dma16((uint32_t)lane * 16, b + ((size_t)((blk >> 4) * KT + kt) * 16 + (blk & 15)) * 1024,
                   lds_addr(st + L::A_BYTES + blk * 1024));
         }
+    }
+    // the first B_PW * bnw weight blocks and all the weight scales
+    __device__ __forceinline__ void issue_b(uint8_t* st, int kt, int lane) const {
+        issue_b_blocks<B_PW, 0>(st, kt, lane);
 #pragma unroll
         for (int i = 0; i < SB_PW; ++i) {
             const int blk = (i * bnw + bw) % L::SB_INSTR;  // 64 columns per instruction
@@ -375,13 +381,14 @@ __device__ __forceinline__ void read_frags(Frags<MI, NI>& f, const uint8_t* st, 
 template <int MI, int NI, int MI0 = 0, int MI1 = MI, bool FIRST = false>
 __device__ __forceinline__ void mfma_blocks(v4f (&acc)[MI][NI], const Frags<MI, NI>& f) {
 #pragma unroll
-    for (int mi = MI0; mi < MI1; ++mi)
+    for (int mi = MI0; mi < MI1; ++mi) {
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
             const v8i b = v8i{f.b[ni][0], f.b[ni][1], f.b[ni][2], f.b[ni][3], 0, 0, 0, 0};
             acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 f.a[mi], b, FIRST ? v4f{0.f, 0.f, 0.f, 0.f} : acc[mi][ni], 0, 4, 0, f.sa[mi], 0, f.sb[ni]);
         }
+    }
 }
 template <int MI, int NI, int MI0 = 0, int MI1 = MI>
 __device__ __forceinline__ void mfma_step(v4f (&acc)[MI][NI], const Frags<MI, NI>& f, bool first) {
@@ -625,12 +632,20 @@ struct CfgPP {
     static constexpr int WTM = SPLIT_ROWS ? 64 : BM;
     static constexpr int WTN = SPLIT_ROWS ? 128 : 64;
     static constexpr int MI = WTM / 16, NI = WTN / 16;
-    static constexpr int B_PW = L::B_INSTR / 4;  // group 0: weights and their scales, + list entry
+    // The weight blocks are split between the groups so that their read phases, which carry the
+    // DMA issue, are about as long: group 0 issues B0_PW weight blocks per wave, the weight
+    // scales and the list entry; group 1 the activation rows and their scales, B1_PW weight
+    // blocks per wave and the row tables.  (Measured on tp_slice: without any weight DMA the
+    // GEMMs ran 13-18% faster, without any row DMA no faster, so the weights-only group was
+    // the one the other waited for.)
+    static constexpr int A_PW = L::A_INSTR >= 4 ? L::A_INSTR / 4 : 1;
+    static constexpr int B_PW = L::B_INSTR / 4;
+    static constexpr int B1_PW = A_PW >= 4 ? B_PW / 4 : B_PW / 2;
+    static constexpr int B0_PW = B_PW - B1_PW;
     static constexpr int SB_PW = L::SB_INSTR / 4;
-    static constexpr int D0 = B_PW + SB_PW + 1;
-    static constexpr int A_PW = L::A_INSTR >= 4 ? L::A_INSTR / 4 : 1;  // group 1: rows, scales, + row tables
+    static constexpr int D0 = B0_PW + SB_PW + 1;
     static constexpr bool GATED = FUSED && !L1;  // + the Linear1 flags of the next tile
-    static constexpr int D1 = A_PW + 1 + 1 + (GATED ? 1 : 0);  // + 1 on the first stage of each tile (Linear1)
+    static constexpr int D1 = A_PW + B1_PW + 1 + 1 + (GATED ? 1 : 0);  // + 1 on the first stage of each tile (Linear1)
     static constexpr int MIN_KT_PERSISTENT = 2 * (L::NS - 1);
     static_assert(2 * D0 < kNoVmWait && 2 * D1 + 1 < kNoVmWait, "vmcnt range");
     static_assert(BM <= 128, "row tables hold 128 rows");
@@ -729,7 +744,7 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
     wait_and_barrier<0>();
 
     if (grp == 0) {
-        StageDma<BM, 512, 1, C::B_PW, C::SB_PW> dma;
+        StageDma<BM, 512, 1, C::B0_PW, C::SB_PW> dma;
         dma.init_b(g, t0, wq, 4);
         // stage s (and the table load that rides with it) for compute step gs = s - (NS - 1)
         auto issue = [&](int s) {
@@ -793,6 +808,7 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
         };
         gate_open(0, t0);
         dma.init_a(g, t0.m, t0.rows, sh.meta[0], L1, wq, 4);
+        dma.init_b(g, t0, wq, 4);
         TileId tn;  // tile whose rows the table load fetches
         read_entry(1, tn);
         // Linear1: byte offset into topk_w of this lane's row of the issued tile
@@ -809,9 +825,11 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
                 read_entry(s / KT, t);
                 gate_open(s / KT, t);
                 dma.init_a(g, t.m, t.rows, sh.meta[(s / KT) % kTableSlots], L1, wq, 4);
+                dma.init_b(g, t, wq, 4);
                 if (L1) w_off = weight_offset(s / KT, t.rows);
             }
             dma.issue_a(sh.smem + (s % L::NS) * L::STAGE, s % KT, lane);
+            dma.template issue_b_blocks<C::B1_PW, 4 * C::B0_PW>(sh.smem + (s % L::NS) * L::STAGE, s % KT, lane);
             load_meta(max(s - (L::NS - 1), 0) / KT + 1, tn);
             if (L1 && s % KT == 0)
                 dma4(w_off, g.topk_w, lds_addr(&sh.wts[(s / KT) % kTableSlots][(wq & 1) * 64]));
