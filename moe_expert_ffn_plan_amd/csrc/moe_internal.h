@@ -20,7 +20,7 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Offsets (bytes) of each table inside a plan workspace.
 // Routing of large inputs runs as three kernels over groups of kRouteTokensPerGroup tokens.
-constexpr int kRouteTokensPerGroup = 256;
+constexpr int kRouteTokensPerGroup = 64;
 
 // Tile widths of the two GEMMs: 512 columns when N allows it, else 256.
 inline int gemm_bn(int n) { return n % 512 == 0 ? 512 : 256; }

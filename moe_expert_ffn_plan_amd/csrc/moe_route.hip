@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kGThreads) void route_count_kernel(const int64_t* _
     extern __shared__ int32_t lds[];
     int32_t* ch = lds;                                          // [E]
     int32_t* cp = lds + E;                                      // [E]
-    int16_t* le = reinterpret_cast<int16_t*>(lds + 2 * E);      // [256 * k]
+    int16_t* le = reinterpret_cast<int16_t*>(lds + 2 * E);      // [kRouteTokensPerGroup * k]
     const int tid = threadIdx.x, g = blockIdx.x;
     for (int i = tid; i < 2 * E; i += kGThreads) lds[i] = 0;
     const int t0 = g * kRouteTokensPerGroup, t1 = min(T, t0 + kRouteTokensPerGroup);
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_kernel(const int64_t*
     extern __shared__ int32_t lds[];
     int32_t* wh = lds;                                           // [kGWaves][E] running hit rows
     int32_t* wp = lds + kGWaves * E;                             // [kGWaves][E] running pull positions
-    int16_t* le = reinterpret_cast<int16_t*>(lds + 2 * kGWaves * E);  // [256 * k]
+    int16_t* le = reinterpret_cast<int16_t*>(lds + 2 * kGWaves * E);  // [kRouteTokensPerGroup * k]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = blockIdx.x;
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     for (int i = tid; i < 2 * kGWaves * E; i += kGThreads) lds[i] = 0;
@@ -544,27 +544,64 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int
     int32_t* gp = gh + E;                   // [E] this group's first pull position (before pbase)
     int32_t* scratch = gp + E;              // [64]
     int32_t* tb = scratch + 64;             // [E+1] M-tile bases
-    int16_t* le = reinterpret_cast<int16_t*>(tb + E + 1);  // [256 * k]
+    int32_t* part = tb + E + 1;             // [4][kGThreads] partial sums of the group-count scan
+    int16_t* le = reinterpret_cast<int16_t*>(part + 4 * kGThreads);  // [kRouteTokensPerGroup * k]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = blockIdx.x;
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     for (int i = tid; i < 2 * kGWaves * E; i += kGThreads) lds[i] = 0;
     const int tg0 = g * kRouteTokensPerGroup, tg1 = min(T, tg0 + kRouteTokensPerGroup);
     load_group_experts(ids, (int64_t)tg0 * k, (int64_t)tg1 * k, k, expert_begin, E, le);
 
-    // ---- scan of the group counts: totals and this group's bases per expert
-    for (int e = tid; e < E; e += kGThreads) {
-        int run = 0, prun = 0, mine = 0, pmine = 0;
-        for (int gg = 0; gg < groups; ++gg) {
-            if (gg == g) { mine = run; pmine = prun; }
-            run += gcounts[(size_t)gg * E + e];
-            prun += gcounts[((size_t)groups + gg) * E + e];
+    // ---- scan of the group counts: totals and this group's bases per expert.  With E <= 256 the
+    // threads split as (expert, slice of the groups), each summing every nsl-th group with several
+    // loads in flight, and the slices are combined through LDS; larger E loop over the experts.
+    {
+        const int nsl = E <= kGThreads ? kGThreads / E : 1;
+        for (int e0 = 0; e0 < E; e0 += kGThreads) {
+            const int e = e0 + (E <= kGThreads ? tid % E : tid), sl = E <= kGThreads ? tid / E : 0;
+            int tot = 0, ptot_ = 0, lt = 0, plt = 0;
+            if (e < E && sl < nsl) {
+                constexpr int kU = 8;  // loads in flight per thread
+                for (int gb = sl; gb < groups; gb += kU * nsl) {
+                    int hc[kU], pc[kU];
+#pragma unroll
+                    for (int u = 0; u < kU; ++u) {
+                        const int gg = gb + u * nsl;
+                        hc[u] = gg < groups ? gcounts[(size_t)gg * E + e] : 0;
+                        pc[u] = gg < groups ? gcounts[((size_t)groups + gg) * E + e] : 0;
+                    }
+#pragma unroll
+                    for (int u = 0; u < kU; ++u) {
+                        const int gg = gb + u * nsl;
+                        tot += hc[u];
+                        ptot_ += pc[u];
+                        if (gg < g) { lt += hc[u]; plt += pc[u]; }
+                    }
+                }
+            }
+            part[tid] = tot;
+            part[kGThreads + tid] = ptot_;
+            part[2 * kGThreads + tid] = lt;
+            part[3 * kGThreads + tid] = plt;
+            __syncthreads();
+            if (tid < min(E - e0, kGThreads)) {
+                int a = 0, b = 0, c = 0, d = 0;
+                for (int q = 0; q < nsl; ++q) {  // slice q of expert e0 + tid sits at thread q * E + tid
+                    const int src = E <= kGThreads ? q * E + tid : tid;
+                    a += part[src];
+                    b += part[kGThreads + src];
+                    c += part[2 * kGThreads + src];
+                    d += part[3 * kGThreads + src];
+                }
+                const int e = e0 + tid;
+                scnt[e] = a;
+                pbase[e + 1] = b;  // pull totals for now
+                gh[e] = c;
+                gp[e] = d;
+            }
+            __syncthreads();
         }
-        scnt[e] = run;
-        gh[e] = mine;
-        gp[e] = pmine;
-        pbase[e + 1] = prun;  // pull totals for now
     }
-    __syncthreads();
     // exclusive scans over experts (E <= 512 = 2 * kGThreads): thread t owns experts 2t and 2t+1
     {
         int padded, pulls, cnt;
@@ -677,7 +714,7 @@ hipError_t launch_route(const moe_shape& s, const int64_t* topk_idx, const PlanP
     hipLaunchKernelGGL(route_count_kernel, dim3(groups), dim3(kGThreads), (size_t)2 * E * 4 + le_bytes, stream,
                        topk_idx, s.num_tokens, s.topk, E, s.expert_begin, groups, p.group_counts);
     if ((int64_t)groups * E <= kFusedScanMaxWords) {
-        const size_t lds = (size_t)(2 * kGWaves * E + 6 * E + 3 + 64) * 4 + le_bytes;
+        const size_t lds = (size_t)(2 * kGWaves * E + 6 * E + 3 + 64 + 4 * kGThreads) * 4 + le_bytes;
         hipLaunchKernelGGL(route_scatter_scan_kernel, dim3(groups), dim3(kGThreads), lds, stream, topk_idx,
                            s.num_tokens, s.topk, E, s.expert_begin, groups, s.block_m, p.group_counts, p);
         return hipGetLastError();
