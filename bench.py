@@ -207,10 +207,10 @@ def main() -> int:
     partial = "true" if w.block_m < bmg else "false"
     if fused:
         k_flops = useful
-        kname = f"Linear1 + Linear2 in one launch (gemm_fused_kernel<{bmg}, {partial}>)"
+        kname = f"Linear1 + Linear2 in one launch (gemm_fused_kernel<{bmg}, {partial}, 0>)"
     else:
         k_flops = 2.0 * n_valid * 2 * I * H
-        kname = "Linear1 grouped GEMM (%s<%d, true, %s>)" % (
+        kname = "Linear1 grouped GEMM (%s<%d, true, %s, 0>)" % (
             "gemm_pp_kernel" if (2 * I) % 512 == 0 else "gemm4_kernel", bmg, partial)
     k_tflops = k_flops / (k_ms * 1e-3) / 1e12
     roofline = {"kernel": kname, "bound": "mfma", "achieved": round(k_tflops, 2),

@@ -63,6 +63,16 @@ enum moe_status {
  *   topk         k, 1..64
  *   block_m      rows per routing block, one of 16, 32, 64, 128; each
  *                expert's rows are padded to a multiple of it.
+ * Linear1 epilogue variants (reading notes, "activation clamp" and the
+ * fast-math switch of the SwiGLU step; walk-through section 4.6):
+ *   swiglu_limit 0: no clamp (the default).  > 0: before SwiGLU the BF16
+ *                gate value is clamped from above, gate = min(gate, limit),
+ *                and the up value on both sides, up = clamp(up, -limit,
+ *                limit) (the pages' default limit is 10).  Must be finite.
+ *   exact_silu   0: silu(g) = g * rcp(1 + exp2(-g log2 e)) with the
+ *                hardware exp2 and reciprocal (the default; the pages'
+ *                fast-math path).  1: g / (1 + expf(-g)) with the accurate
+ *                library expf and IEEE division.
  */
 typedef struct moe_shape {
     int32_t num_tokens;
@@ -72,6 +82,8 @@ typedef struct moe_shape {
     int32_t expert_begin;
     int32_t topk;
     int32_t block_m;
+    float swiglu_limit;
+    int32_t exact_silu;
 } moe_shape;
 
 /* Worst-case padded row count of the routing layout ("pool capacity"):

@@ -27,7 +27,7 @@ class MoeError(RuntimeError):
 class MoeShape(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("intermediate", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("expert_begin", ctypes.c_int32), ("topk", ctypes.c_int32),
-                ("block_m", ctypes.c_int32)]
+                ("block_m", ctypes.c_int32), ("swiglu_limit", ctypes.c_float), ("exact_silu", ctypes.c_int32)]
 
 
 class PlanView(ctypes.Structure):
@@ -80,14 +80,16 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def make_shape(num_tokens, hidden, intermediate, num_experts, topk, block_m, expert_begin=0) -> MoeShape:
-    return MoeShape(num_tokens, hidden, intermediate, num_experts, expert_begin, topk, block_m)
+def make_shape(num_tokens, hidden, intermediate, num_experts, topk, block_m, expert_begin=0, swiglu_limit=0.0,
+               exact_silu=False) -> MoeShape:
+    return MoeShape(num_tokens, hidden, intermediate, num_experts, expert_begin, topk, block_m, float(swiglu_limit),
+                    int(bool(exact_silu)))
 
 
-def shape_of(workload, num_tokens=None, expert_begin=0) -> MoeShape:
+def shape_of(workload, num_tokens=None, expert_begin=0, swiglu_limit=0.0, exact_silu=False) -> MoeShape:
     w = workload
     return make_shape(w.num_tokens if num_tokens is None else num_tokens, w.hidden, w.intermediate,
-                      w.num_experts, w.topk, w.block_m, expert_begin)
+                      w.num_experts, w.topk, w.block_m, expert_begin, swiglu_limit, exact_silu)
 
 
 def _check(fn, status):

@@ -31,6 +31,8 @@ int check_shape(const moe_shape* s) {
     if (s->topk < 1 || s->topk > kMaxTopk) return MOE_ERR_SHAPE;
     if (!(s->block_m == 16 || s->block_m == 32 || s->block_m == 64 || s->block_m == 128)) return MOE_ERR_SHAPE;
     if ((int64_t)s->num_tokens * s->topk >= (1ll << 30)) return MOE_ERR_SHAPE;
+    if (!(s->swiglu_limit >= 0.0f && s->swiglu_limit <= 3.0e38f)) return MOE_ERR_SHAPE;  // also rejects NaN
+    if (s->exact_silu != 0 && s->exact_silu != 1) return MOE_ERR_SHAPE;
     if (s->hidden > (1 << 20) || s->intermediate > (1 << 20)) return MOE_ERR_SHAPE;
     if (s->hidden % 256 != 0 || s->intermediate % 128 != 0) return MOE_ERR_ALIGN;
     // kernels address each operand's rows with 32-bit offsets

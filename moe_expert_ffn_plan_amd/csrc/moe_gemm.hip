@@ -87,6 +87,8 @@ struct GemmArgs {
     uint16_t* out_bf16;     // Linear2: [cap, N]
     int K, N, topk;
     int bm_shift;           // log2 of the routing block (bm) that the scale layout uses
+    float swiglu_limit;     // Linear1: > 0 clamps gate from above and up on both sides before SwiGLU
+    int exact_silu;         // Linear1: 1 = accurate expf and IEEE division in SiLU
     int count_idx;          // scalars[count_idx] = tiles in the list
 };
 
@@ -406,7 +408,11 @@ __device__ __forceinline__ void mfma_step(v4f (&acc)[MI][NI], const Frags<MI, NI
 // otherwise every tile has BM valid rows and the row checks compile away.
 // COHERENT: the stores are device-scope (sc1) stores, complete at device scope
 // once vmcnt has drained (the fused launch hands these rows to other XCDs).
-template <int BM, int MI, int NI, bool PARTIAL, bool COHERENT>
+// Linear1 epilogue variants: kEpiFast (hardware exp2/rcp, no clamp; the default), kEpiClamp (the same
+// with the activation clamp), kEpiExact (accurate expf and IEEE division, clamp if the limit is > 0).
+constexpr int kEpiFast = 0, kEpiClamp = 1, kEpiExact = 2;
+
+template <int BM, int MI, int NI, bool PARTIAL, bool COHERENT, int EPI>
 __device__ __forceinline__ void epilogue_linear1(const v4f (&acc)[MI][NI], const GemmArgs& g, int m0, int rows,
                                                  int wrow0, int gcol0, const float* row_w, const int* row_tok,
                                                  int lane) {
@@ -439,10 +445,17 @@ __device__ __forceinline__ void epilogue_linear1(const v4f (&acc)[MI][NI], const
                     // gate and up rounded to BF16 together, then widened back to FP32
                     const uint32_t gu = pack_bf16(gate_lane ? acc[mi][grp * 4 + b][ii] : other[b][2 + ii],
                                                   gate_lane ? other[b][ii] : acc[mi][grp * 4 + b][2 + ii]);
-                    const float gv = __uint_as_float(gu << 16);
-                    const float uv = __uint_as_float(gu & 0xFFFF0000u);
-                    // silu(g) = g / (1 + 2^(-g log2 e)) with the hardware exp2 and reciprocal
-                    const float s = gv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv * kLog2e));
+                    float gv = __uint_as_float(gu << 16);
+                    float uv = __uint_as_float(gu & 0xFFFF0000u);
+                    if (EPI == kEpiClamp || (EPI == kEpiExact && g.swiglu_limit > 0.0f)) {  // activation clamp
+                        gv = fminf(gv, g.swiglu_limit);
+                        uv = fminf(fmaxf(uv, -g.swiglu_limit), g.swiglu_limit);
+                    }
+                    // silu(g) = g / (1 + 2^(-g log2 e)) with the hardware exp2 and reciprocal, or with
+                    // the accurate expf and IEEE division
+                    const float s = EPI == kEpiExact
+                                        ? gv / (1.0f + expf(-gv))
+                                        : gv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv * kLog2e));
                     h[b] = (s * uv) * wgt;
                     amax = fmaxf(amax, fabsf(h[b]));
                 }
@@ -495,11 +508,12 @@ __device__ __forceinline__ void epilogue_linear2(const v4f (&acc)[MI][NI], const
         }
 }
 
-template <int BM, int MI, int NI, bool L1, bool PARTIAL, bool COHERENT = false>
+template <int BM, int MI, int NI, bool L1, bool PARTIAL, bool COHERENT = false, int EPI = kEpiFast>
 __device__ __forceinline__ void epilogue(const v4f (&acc)[MI][NI], const GemmArgs& g, const TileId& t, int wrow0,
                                          int gcol0, const float* row_w, const int* row_tok, int lane) {
     if constexpr (L1)
-        epilogue_linear1<BM, MI, NI, PARTIAL, COHERENT>(acc, g, t.m, t.rows, wrow0, gcol0, row_w, row_tok, lane);
+        epilogue_linear1<BM, MI, NI, PARTIAL, COHERENT, EPI>(acc, g, t.m, t.rows, wrow0, gcol0, row_w, row_tok,
+                                                             lane);
     else epilogue_linear2<BM, MI, NI, PARTIAL>(acc, g, t.m, t.rows, wrow0, gcol0, row_tok, lane);
 }
 
@@ -532,7 +546,7 @@ struct Cfg4 {
     static_assert(2 * D < 64, "vmcnt range");
 };
 
-template <int BM, bool L1, bool PARTIAL>
+template <int BM, bool L1, bool PARTIAL, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
     using C = Cfg4<BM>;
     using L = typename C::L;
@@ -568,7 +582,7 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
         read_frags<BM, 256>(f, smem + (kt % L::NS) * L::STAGE, wrow0, wcol0, lane);
         mfma_step(acc, f, kt == 0);
     }
-    epilogue<BM, C::MI, C::NI, L1, PARTIAL>(acc, g, t, wrow0, t.n * 256 + wcol0, row_w, row_tok, lane);
+    epilogue<BM, C::MI, C::NI, L1, PARTIAL, false, EPI>(acc, g, t, wrow0, t.n * 256 + wcol0, row_w, row_tok, lane);
 }
 
 // ============================================================================
@@ -681,7 +695,7 @@ struct TileSeq {
 };
 
 // One persistent run over the tiles `seq` of g's list.
-template <int BM, bool L1, bool PARTIAL, bool FUSED>
+template <int BM, bool L1, bool PARTIAL, bool FUSED, int EPI>
 __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync, const TileSeq& seq,
                                        PPShared<BM>& sh) {
     const int ntiles = seq.n;
@@ -775,7 +789,7 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
             mfma_step<C::MI, C::NI, 0, MH>(acc, f, kt == 0);
             mfma_step<C::MI, C::NI, MH, C::MI>(acc, f, kt == 0);
             if (++kt == KT) {
-                epilogue<BM, C::MI, C::NI, L1, PARTIAL, FUSED>(acc, g, ct, wrow0, ct.n * 512 + wcol0,
+                epilogue<BM, C::MI, C::NI, L1, PARTIAL, FUSED, EPI>(acc, g, ct, wrow0, ct.n * 512 + wcol0,
                                                                sh.wts[ci % kTableSlots], sh.meta[ci % kTableSlots],
                                                                lane);
                 if constexpr (FUSED && L1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // stores complete
@@ -866,7 +880,7 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
             }
             mfma_step(acc, f, kt == 0);
             if (++kt == KT) {
-                epilogue<BM, C::MI, C::NI, L1, PARTIAL, FUSED>(acc, g, ct, wrow0, ct.n * 512 + wcol0,
+                epilogue<BM, C::MI, C::NI, L1, PARTIAL, FUSED, EPI>(acc, g, ct, wrow0, ct.n * 512 + wcol0,
                                                                sh.wts[ci % kTableSlots], sh.meta[ci % kTableSlots],
                                                                lane);
                 if constexpr (FUSED && L1) {
@@ -892,14 +906,14 @@ __device__ __forceinline__ TileSeq round_robin(int begin, int end, int slot, int
     return TileSeq{first, n, nslots, 0, 1, n};
 }
 
-template <int BM, bool L1, bool PARTIAL>
+template <int BM, bool L1, bool PARTIAL, int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
     __shared__ PPShared<BM> sh;
     int begin, end;
     xcd_chunk(g, g.N / 512, blockIdx.x % kNumXcd, begin, end);
     const TileSeq seq = round_robin(begin, end, blockIdx.x / kNumXcd, gridDim.x / kNumXcd);
     if (seq.n == 0) return;
-    pp_run<BM, L1, PARTIAL, false>(g, FusedSync{}, seq, sh);
+    pp_run<BM, L1, PARTIAL, false, EPI>(g, FusedSync{}, seq, sh);
 }
 
 struct FusedArgs {
@@ -913,7 +927,7 @@ struct FusedArgs {
 // light workgroups run the first L * d Linear2 tiles (d = Linear2 tiles per Linear1 tile of time,
 // from the K-steps; the list runs M-tile by M-tile, so these need the M-tiles the first Linear1
 // round computed); the rest go round-robin to all workgroups.
-template <int BM, bool PARTIAL>
+template <int BM, bool PARTIAL, int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_fused_kernel(FusedArgs fa) {
     __shared__ PPShared<BM> sh;
     const int nslots = gridDim.x / kNumXcd, xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
@@ -921,7 +935,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fused_kernel(FusedArgs fa) {
     xcd_chunk(fa.g1, fa.g1.N / 512, xcd, b1, e1);
     xcd_chunk(fa.g2, fa.g2.N / 512, xcd, b2, e2);
     const TileSeq s1 = round_robin(b1, e1, slot, nslots);
-    if (s1.n > 0) pp_run<BM, true, PARTIAL, true>(fa.g1, fa.sync, s1, sh);
+    if (s1.n > 0) pp_run<BM, true, PARTIAL, true, EPI>(fa.g1, fa.sync, s1, sh);
     wait_and_barrier<0>();  // the Linear1 run's table loads have landed before the tables are reused
 
     const int r1 = (e1 - b1) % nslots, nl = r1 > 0 ? nslots - r1 : 0;  // light workgroups: slots >= r1
@@ -936,7 +950,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fused_kernel(FusedArgs fa) {
     s2.first_b = b2 + na_all + slot;
     s2.stride_b = nslots;
     s2.n = s2.n_a + (s2.first_b < e2 ? (e2 - s2.first_b + nslots - 1) / nslots : 0);
-    if (s2.n > 0) pp_run<BM, false, PARTIAL, true>(fa.g2, fa.sync, s2, sh);
+    if (s2.n > 0) pp_run<BM, false, PARTIAL, true, kEpiFast>(fa.g2, fa.sync, s2, sh);
 }
 
 // Compute units of the current device (cached per device).
@@ -966,16 +980,38 @@ int64_t persistent_grid(int64_t all) {
     return std::max<int64_t>(kNumXcd, std::min(all, cus));
 }
 
+template <int BM, bool L1, bool PARTIAL, int EPI>
+hipError_t launch_bm_epi(const GemmArgs& args, int64_t all, hipStream_t stream) {
+    if (gemm_bn(args.N) == 512) {
+        const int64_t grid = args.K / kBK >= min_kt_persistent(BM) ? persistent_grid(all) : all;
+        hipLaunchKernelGGL((gemm_pp_kernel<BM, L1, PARTIAL, EPI>), dim3(grid), dim3(512), 0, stream, args);
+    } else {
+        hipLaunchKernelGGL((gemm4_kernel<BM, L1, PARTIAL, EPI>), dim3(all), dim3(256), 0, stream, args);
+    }
+    return hipGetLastError();
+}
+
+// Linear1 epilogue variant of a problem
+int epi_of(const GemmArgs& a) { return a.exact_silu ? kEpiExact : a.swiglu_limit > 0.0f ? kEpiClamp : kEpiFast; }
+
+template <int BM, bool PARTIAL>
+void launch_fused(int epi, dim3 grid, dim3 block, hipStream_t stream, const FusedArgs& fa) {
+    if (epi == kEpiClamp) hipLaunchKernelGGL((gemm_fused_kernel<BM, PARTIAL, kEpiClamp>), grid, block, 0, stream, fa);
+    else if (epi == kEpiExact) hipLaunchKernelGGL((gemm_fused_kernel<BM, PARTIAL, kEpiExact>), grid, block, 0, stream, fa);
+    else hipLaunchKernelGGL((gemm_fused_kernel<BM, PARTIAL, kEpiFast>), grid, block, 0, stream, fa);
+}
+
 // all: workgroups for one tile each
 template <int BM, bool L1, bool PARTIAL>
 hipError_t launch_bm(const GemmArgs& args, int64_t all, hipStream_t stream) {
-    if (gemm_bn(args.N) == 512) {
-        const int64_t grid = args.K / kBK >= min_kt_persistent(BM) ? persistent_grid(all) : all;
-        hipLaunchKernelGGL((gemm_pp_kernel<BM, L1, PARTIAL>), dim3(grid), dim3(512), 0, stream, args);
-    } else {
-        hipLaunchKernelGGL((gemm4_kernel<BM, L1, PARTIAL>), dim3(all), dim3(256), 0, stream, args);
+    if constexpr (L1) {
+        switch (epi_of(args)) {
+            case kEpiClamp: return launch_bm_epi<BM, true, PARTIAL, kEpiClamp>(args, all, stream);
+            case kEpiExact: return launch_bm_epi<BM, true, PARTIAL, kEpiExact>(args, all, stream);
+            default: return launch_bm_epi<BM, true, PARTIAL, kEpiFast>(args, all, stream);
+        }
     }
-    return hipGetLastError();
+    return launch_bm_epi<BM, L1, PARTIAL, kEpiFast>(args, all, stream);
 }
 
 // Workgroups for one tile each of a GEMM with N columns: every XCD gets the slots of ceil(M-tiles / 8)
@@ -1014,6 +1050,8 @@ GemmArgs common_args(const GemmProblem& p) {
     a.row_topk = p.plan->row_topk;
     a.topk = p.shape->topk;
     a.bm_shift = 31 - __builtin_clz((unsigned)p.shape->block_m);
+    a.swiglu_limit = p.shape->swiglu_limit;
+    a.exact_silu = p.shape->exact_silu;
     return a;
 }
 
@@ -1081,9 +1119,10 @@ hipError_t launch_expert_ffn(const GemmProblem& p, const uint8_t* x, const uint8
     if (tiles == 0) return hipSuccess;
     const dim3 grid((unsigned)persistent_grid(tiles)), block(512);
     const int bm = p.shape->block_m, bmg = gemm_bm(bm);
-    if (bmg == 16) hipLaunchKernelGGL((gemm_fused_kernel<16, false>), grid, block, 0, stream, fa);
-    else if (bm == 128) hipLaunchKernelGGL((gemm_fused_kernel<128, false>), grid, block, 0, stream, fa);
-    else hipLaunchKernelGGL((gemm_fused_kernel<128, true>), grid, block, 0, stream, fa);
+    const int epi = epi_of(fa.g1);
+    if (bmg == 16) launch_fused<16, false>(epi, grid, block, stream, fa);
+    else if (bm == 128) launch_fused<128, false>(epi, grid, block, stream, fa);
+    else launch_fused<128, true>(epi, grid, block, stream, fa);
     return hipGetLastError();
 }
 

@@ -15,7 +15,9 @@ Steps, in the order the pages give them:
    notes "SwiGLU computation"): gate and up accumulators rounded to BF16 and
    read back as float, silu(g) = g / (1 + exp(-g)), then h = (silu(g) * u) * w
    with two float32 multiplies in that order.  The optional activation clamp
-   is off.
+   (reading notes, "activation clamp": the gate path bounded from above, the
+   up path on both sides, default threshold 10) is applied to the BF16 values
+   before silu when a limit > 0 is given; by default it is off.
 4. Requant (reading notes, "amax, scale factor and FP8 intermediate"): per
    row and 32-channel group, amax = max |h|; a power-of-two UE8M0 scale (rule
    in ``formats.requant_scale_code``); q = E4M3 round-to-nearest-even of
@@ -68,14 +70,19 @@ def silu_f32(g: np.ndarray) -> np.ndarray:
         return (g64 / (1.0 + np.exp(-g64))).astype(np.float32)
 
 
-def swiglu_weight(z_gate: np.ndarray, z_up: np.ndarray, w: np.ndarray) -> np.ndarray:
-    """h = fl32(fl32(silu(bf16(g)) * bf16(u)) * w); w broadcasts per row.
+def swiglu_weight(z_gate: np.ndarray, z_up: np.ndarray, w: np.ndarray, limit: float = 0.0) -> np.ndarray:
+    """h = fl32(fl32(silu(bf16(g)) * bf16(u)) * w); w broadcasts per row.  With limit > 0,
+    g = min(bf16(g), limit) and u = clip(bf16(u), -limit, limit) first.
 
     Parity unpinned beyond this closed form: the pages print no numeric
     example of the epilogue.
     """
     g = F.bf16_rne(z_gate)
     u = F.bf16_rne(z_up)
+    if limit > 0:
+        lim = np.float32(limit)
+        g = np.minimum(g, lim)
+        u = np.clip(u, -lim, lim)
     s = silu_f32(g)
     su = (s * u).astype(np.float32)
     w32 = np.asarray(w, np.float32)
@@ -105,19 +112,19 @@ def combine(yslot_vals: np.ndarray, slot: np.ndarray) -> np.ndarray:
     return F.bf16_rne(acc)
 
 
-def expert_rows_forward(xq_rows, xsf_rows, w_rows, w1, w1_sf, w2, w2_sf):
+def expert_rows_forward(xq_rows, xsf_rows, w_rows, w1, w1_sf, w2, w2_sf, swiglu_limit: float = 0.0):
     """Rows of one expert: FP8 activations [n, H] -> (H_q, H_sf, Yslot BF16 values)."""
     a = dequant_fp8_rows(xq_rows, xsf_rows)
     z = matmul_f32(a, dequant_fp4_rows(w1, w1_sf))
     gate, up = deinterleave_gate_up(z)
-    h = swiglu_weight(gate, up, w_rows)
+    h = swiglu_weight(gate, up, w_rows, swiglu_limit)
     hq, hsf = requant_fp8(h)
     y2 = matmul_f32(dequant_fp8_rows(hq, hsf), dequant_fp4_rows(w2, w2_sf))
     return hq, hsf, F.bf16_rne(y2)
 
 
 def forward_ref(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, *, num_experts: int,
-                expert_begin: int, block_m: int, plan: Plan | None = None):
+                expert_begin: int, block_m: int, plan: Plan | None = None, swiglu_limit: float = 0.0):
     """Whole forward.  Returns a dict with the plan, H_q/H_sf/Yslot over [R_pad] rows and y.
 
     Shapes: x uint8 [T, H] (E4M3), x_sf uint8 [T, H/32], topk_idx int64 [T, k],
@@ -139,14 +146,15 @@ def forward_ref(x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, *, num_experts:
             continue
         rows = np.arange(r0, r0 + n)
         tok, j = plan.row_token[rows], plan.row_topk[rows]
-        q, s, yv = expert_rows_forward(x[tok], x_sf[tok], tw[tok, j], w1[e], w1_sf[e], w2[e], w2_sf[e])
+        q, s, yv = expert_rows_forward(x[tok], x_sf[tok], tw[tok, j], w1[e], w1_sf[e], w2[e], w2_sf[e],
+                                       swiglu_limit)
         hq[rows], hsf[rows], ys[rows] = q, s, yv
     y = combine(ys, plan.slot)
     return {"plan": plan, "h_q": hq, "h_sf": hsf, "yslot": ys, "y": y}
 
 
 def forward_tokens(tokens, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, *,
-                   num_experts: int, expert_begin: int):
+                   num_experts: int, expert_begin: int, swiglu_limit: float = 0.0):
     """y rows (BF16 values as float32) for a subset of tokens only.
 
     Each token's rows are independent of every other token's, so the result
@@ -169,7 +177,8 @@ def forward_tokens(tokens, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, *,
     for e, hits in by_expert.items():
         tt = np.array([h[0] for h in hits])
         jj = np.array([h[1] for h in hits])
-        q, s, yv = expert_rows_forward(x[tt], x_sf[tt], tw[tt, jj], w1[e], w1_sf[e], w2[e], w2_sf[e])
+        q, s, yv = expert_rows_forward(x[tt], x_sf[tt], tw[tt, jj], w1[e], w1_sf[e], w2[e], w2_sf[e],
+                                       swiglu_limit)
         for i, h in enumerate(hits):
             per_hit[h] = (q[i], s[i], yv[i])
     y = np.zeros((tokens.size, H), np.float32)

@@ -18,9 +18,9 @@ from parity import (assert_fp8_gate, assert_plan_equal, assert_y_gate, bf16_to_f
 pytestmark = pytest.mark.gpu
 
 
-def run_gpu(w, d, dev, expert_begin=0, separate_plan=True):
+def run_gpu(w, d, dev, expert_begin=0, separate_plan=True, swiglu_limit=0.0, exact_silu=False):
     T = d["x"].shape[0]
-    s = B.shape_of(w, num_tokens=T, expert_begin=expert_begin)
+    s = B.shape_of(w, num_tokens=T, expert_begin=expert_begin, swiglu_limit=swiglu_limit, exact_silu=exact_silu)
     g = {k: v.to(dev) for k, v in d.items()}
     g.update(B.prepare_all(s, g))
     y = torch.full((T, w.hidden), -1, dtype=torch.int16, device=dev)
@@ -38,10 +38,11 @@ def run_gpu(w, d, dev, expert_begin=0, separate_plan=True):
             "plan": gpu_plan_to_numpy(pv, T, w.topk)}
 
 
-def check_full(w, d_cpu, out, expert_begin=0):
+def check_full(w, d_cpu, out, expert_begin=0, swiglu_limit=0.0):
     d = inputs.to_numpy(d_cpu)
     ref = forward_ref(d["x"], d["x_sf"], d["topk_idx"] - expert_begin, d["topk_w"], d["w1"], d["w1_sf"], d["w2"],
-                      d["w2_sf"], num_experts=w.num_experts, expert_begin=0, block_m=w.block_m)
+                      d["w2_sf"], num_experts=w.num_experts, expert_begin=0, block_m=w.block_m,
+                      swiglu_limit=swiglu_limit)
     p = ref["plan"]
     assert_plan_equal(out["plan"], plan_ref(d["topk_idx"], w.num_experts, expert_begin, w.block_m))
     valid = p.row_token >= 0
@@ -78,6 +79,31 @@ def test_forward_small_full(gpu, name):
     d = inputs.make_inputs(w, device="cpu")
     out = run_gpu(w, d, gpu)
     check_full(w, d, out)
+
+
+# Linear1 epilogue variants (activation clamp, accurate SiLU) on inputs with x * 50 outliers, so
+# that the clamp at 10 changes many values; block_m 128 runs two launches, block_m 32 the single one.
+EPILOGUE_CASES = {
+    "out_bm128": inputs.Workload("out_bm128", 700, 1024, 256, 8, 64, 8, 128, "zipf", 0.2, 50.0, seed=16,
+                                 weight_seed=26),
+    "out_bm32": inputs.Workload("out_bm32", 500, 1024, 512, 8, 12, 4, 32, "uniform", 0.2, 50.0, seed=17,
+                                weight_seed=27),
+}
+
+
+@pytest.mark.parametrize("name", list(EPILOGUE_CASES))
+@pytest.mark.parametrize("limit,exact", [(10.0, False), (0.0, True), (10.0, True)])
+def test_forward_epilogue_variants(gpu, name, limit, exact):
+    w = EPILOGUE_CASES[name]
+    print(f"forward parity: {name} swiglu_limit={limit} exact_silu={exact}", flush=True)
+    d = inputs.make_inputs(w, device="cpu")
+    out = run_gpu(w, d, gpu, swiglu_limit=limit, exact_silu=exact)
+    ref = check_full(w, d, out, swiglu_limit=limit)
+    if limit > 0:  # the clamp is active on these inputs
+        dn = inputs.to_numpy(d)
+        plain = forward_ref(dn["x"], dn["x_sf"], dn["topk_idx"], dn["topk_w"], dn["w1"], dn["w1_sf"], dn["w2"],
+                            dn["w2_sf"], num_experts=w.num_experts, expert_begin=0, block_m=w.block_m)
+        assert not np.array_equal(plain["h_q"], ref["h_q"])
 
 
 def test_forward_internal_plan_and_expert_begin(gpu):

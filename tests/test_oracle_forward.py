@@ -188,3 +188,46 @@ def test_single_expert_dense_ffn():
                     num_experts=1, expert_begin=0, block_m=16)
     for t in range(w.num_tokens):
         assert np.array_equal(r["y"][t], reference_token(t, d, 1))
+
+
+def test_swiglu_clamp_closed_form():
+    # activation clamp (reading notes, "activation clamp"): gate bounded above, up on both sides;
+    # expected values from math.exp on Python floats, rounded to float32 step by step
+    import math
+    from oracle.forward import swiglu_weight
+    cases = [  # (gate, up, w, limit)
+        (20.0, -30.0, 0.5, 10.0),    # both clamped
+        (-30.0, 4.0, 1.0, 10.0),     # gate below -limit is not clamped
+        (3.0, 12.5, 2.0, 10.0),      # up clamped from above only
+        (10.0, -10.0, 1.0, 10.0),    # exactly at the limit
+        (7.0, 2.0, 0.25, 0.0),       # limit 0: no clamp
+    ]
+    for g, u, wt, lim in cases:
+        h = swiglu_weight(np.array([[g]], np.float32), np.array([[u]], np.float32), np.array([wt], np.float32), lim)
+        gc = min(g, lim) if lim > 0 else g
+        uc = max(-lim, min(u, lim)) if lim > 0 else u
+        s = np.float32(gc / (1.0 + math.exp(-gc)))
+        expect = np.float32(np.float32(s * np.float32(uc)) * np.float32(wt))
+        assert h[0, 0] == expect, (g, u, wt, lim, h[0, 0], expect)
+
+
+def test_swiglu_clamp_bounds_and_identity(tiny):
+    from oracle.forward import swiglu_weight
+    rng = np.random.default_rng(5)
+    zg = (rng.standard_normal((64, 96)) * 40).astype(np.float32)
+    zu = (rng.standard_normal((64, 96)) * 40).astype(np.float32)
+    wt = rng.random(64).astype(np.float32)
+    plain = swiglu_weight(zg, zu, wt)
+    # a limit above every value changes nothing (bit for bit)
+    assert np.array_equal(swiglu_weight(zg, zu, wt, 1e30), plain)
+    # with limit L: |h| <= max(L, max |silu| on the negative axis) * L * w
+    L = 3.0
+    h = swiglu_weight(zg, zu, wt, L)
+    assert np.all(np.abs(h) <= max(L, 0.2785) * L * wt[:, None] * (1 + 1e-6))
+    assert not np.array_equal(h, plain)
+    # the whole forward: a clamp at 1e30 is the unclamped forward
+    w, d = tiny
+    r0 = run(w, d)
+    r1 = forward_ref(d["x"], d["x_sf"], d["topk_idx"], d["topk_w"], d["w1"], d["w1_sf"], d["w2"], d["w2_sf"],
+                     num_experts=w.num_experts, expert_begin=0, block_m=w.block_m, swiglu_limit=1e30)
+    assert np.array_equal(r0["y"], r1["y"]) and np.array_equal(r0["h_q"], r1["h_q"])
