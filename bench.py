@@ -25,6 +25,7 @@ oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -99,6 +100,10 @@ def main() -> int:
                     help="run Linear1 and Linear2 through moe_expert_ffn (one launch) wherever it is supported")
     ap.add_argument("--host-inputs", action="store_true",
                     help="draw the synthetic inputs on the CPU and copy them (fewer torch GPU kernels, for profilers)")
+    ap.add_argument("--block-m", type=int, default=0,
+                    help="routing block rows to use instead of the workload's own (16, 32, 64 or 128)")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="number of tokens to use instead of the workload's own (same routing recipe)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain elementwise copy (y = -x, float32) of this many MiB five times: the "
                          "reference kernel for scaling HBM byte counters")
@@ -126,6 +131,12 @@ def main() -> int:
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "dispatches": 5}), flush=True)
         return 0
     w = inputs.WORKLOADS[args.workload]
+    if args.block_m:
+        w = dataclasses.replace(w, block_m=args.block_m)
+    if args.tokens:
+        w = dataclasses.replace(w, num_tokens=args.tokens)
+    if args.block_m or args.tokens:  # a different workload: no committed profile describes it
+        w = dataclasses.replace(w, name=f"{w.name}_T{w.num_tokens}_bm{w.block_m}")
     s = B.shape_of(w)
     gen_dev = "cpu" if args.host_inputs else dev
     d = {k: v.to(dev) for k, v in inputs.make_inputs(w, device=gen_dev).items()}

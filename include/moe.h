@@ -93,6 +93,32 @@ typedef struct moe_shape {
  * for k <= E.  Returns MOE_OK and writes *rows, or an error status. */
 MOE_API int moe_capacity_rows(const moe_shape* shape, int64_t* rows);
 
+/* Routing block heuristic (walk-through section 7.1, "BLOCK_M selection"):
+ * the expected rows per expert, num_tokens * topk / num_experts, times the
+ * pages' imbalance factor 2 is the target; the result is the smallest
+ * supported block_m (16, 32, 64, 128) that is >= the target, else 128.
+ *   num_tokens   tokens whose top-k lists are routed (all ranks' tokens,
+ *                num_tokens x num_ranks in the pages' formula), >= 0
+ *   topk         k, 1..64
+ *   num_experts  experts the ids are drawn from (all ranks' experts), >= 1
+ * Host only.  Returns MOE_OK and writes *block_m, MOE_ERR_NULL, or
+ * MOE_ERR_SHAPE for arguments out of range (num_tokens < 2^40). */
+MOE_API int moe_suggest_block_m(int64_t num_tokens, int32_t topk, int32_t num_experts,
+                int32_t* block_m);
+
+/* How many GEMM launches moe_expert_ffn and moe_forward make for this
+ * shape on the current device: *expert_ffn = 1 if moe_expert_ffn runs
+ * Linear1 and Linear2 as one persistent launch (see there), 2 if it falls
+ * back to moe_linear1 + moe_linear2; *forward = 1 if moe_forward runs
+ * moe_expert_ffn as one launch, 2 if it runs moe_linear1 + moe_linear2.
+ * moe_forward takes the one launch when moe_expert_ffn supports it and
+ * Linear1 has at most 16 tiles per compute unit in the worst case (every
+ * hit local), bounded by (cap / M + E) * (2I / 512) tiles, M = 16 for
+ * block_m 16, else 128, cap as in moe_capacity_rows (integer division).  Host only (the
+ * compute-unit count of the current device; 256 if there is none).
+ * Returns MOE_OK, MOE_ERR_NULL or a shape error. */
+MOE_API int moe_gemm_launches(const moe_shape* shape, int32_t* expert_ffn, int32_t* forward);
+
 /* ---- routing tables ------------------------------------------------------
  * What is built follows the practice page's schedule tables (section 2) and
  * the MegaMoE dispatch counting (walk-through section 4.2, steps 1 and 3):
@@ -200,14 +226,13 @@ MOE_API int moe_forward(const moe_shape* shape,
 
 /* ---- the forward's stages (Linear1 gathers its rows, their scales and the
  * top-k weights through the plan's row tables itself) ------------------------
- * moe_forward(plan_ws != NULL) is exactly moe_expert_ffn (for block_m < 128)
- * or moe_linear1 then moe_linear2 (block_m = 128), then moe_combine, in this
- * order on one stream; moe_expert_ffn computes what moe_linear1 then
+ * moe_forward(plan_ws != NULL) is exactly moe_expert_ffn or moe_linear1 then
+ * moe_linear2 (the choice moe_gemm_launches reports), then moe_combine, in
+ * this order on one stream; moe_expert_ffn computes what moe_linear1 then
  * moe_linear2 compute (bit for bit), in one persistent launch where the
- * shape allows it.  (Small routing blocks mean few rows per expert and few
- * tiles per CU, where the single launch saves a kernel tail and ramp; with
- * many tiles per CU it measured slightly slower.)  They are exposed so a
- * caller can schedule or time the stages itself.  Arguments mean what they mean for moe_forward; plan_ws
+ * shape allows it.  (With few Linear1 tiles per CU the single launch saves a
+ * kernel tail and ramp; with many it measured slightly slower.)  They are
+ * exposed so a caller can schedule or time the stages itself.  Arguments mean what they mean for moe_forward; plan_ws
  * (from moe_plan) is required here, and ws must be the same forward
  * workspace for all of them.
  *   moe_linear1: grouped Linear1 over the routing layout with the fused

@@ -43,7 +43,7 @@ class ForwardView(ctypes.Structure):
 
 _lib = None
 
-EXPORTS = ["moe_capacity_rows", "moe_plan_workspace_bytes", "moe_plan", "moe_plan_view_get",
+EXPORTS = ["moe_capacity_rows", "moe_suggest_block_m", "moe_gemm_launches", "moe_plan_workspace_bytes", "moe_plan", "moe_plan_view_get",
            "moe_forward_workspace_bytes", "moe_forward", "moe_linear1", "moe_linear2", "moe_combine",
            "moe_expert_ffn", "moe_prepare_weights",
            "moe_forward_view_get", "moe_device_supported", "moe_status_str"]
@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         P, VP, SZ = ctypes.POINTER, ctypes.c_void_p, ctypes.c_size_t
         S = P(MoeShape)
         L.moe_capacity_rows.argtypes = [S, P(ctypes.c_int64)]
+        L.moe_suggest_block_m.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P(ctypes.c_int32)]
+        L.moe_gemm_launches.argtypes = [S, P(ctypes.c_int32), P(ctypes.c_int32)]
         L.moe_plan_workspace_bytes.argtypes = [S, P(SZ)]
         L.moe_forward_workspace_bytes.argtypes = [S, P(SZ)]
         L.moe_plan.argtypes = [S, VP, VP, SZ, VP]
@@ -125,6 +127,20 @@ def capacity_rows(shape: MoeShape) -> int:
     v = ctypes.c_int64()
     _check("moe_capacity_rows", lib().moe_capacity_rows(ctypes.byref(shape), ctypes.byref(v)))
     return v.value
+
+
+def suggest_block_m(num_tokens: int, topk: int, num_experts: int) -> int:
+    """moe_suggest_block_m: routing block rows for num_tokens tokens routed top-k over num_experts experts."""
+    v = ctypes.c_int32()
+    _check("moe_suggest_block_m", lib().moe_suggest_block_m(num_tokens, topk, num_experts, ctypes.byref(v)))
+    return v.value
+
+
+def gemm_launches(shape: MoeShape) -> tuple[int, int]:
+    """moe_gemm_launches: (GEMM launches of moe_expert_ffn, GEMM launches of moe_forward), 1 or 2 each."""
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    _check("moe_gemm_launches", lib().moe_gemm_launches(ctypes.byref(shape), ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
 
 
 def plan_workspace_bytes(shape: MoeShape) -> int:
@@ -234,17 +250,13 @@ def expert_ffn(shape: MoeShape, x, x_sf, topk_w, w1, w1_sf, w2, w2_sf, plan_ws, 
 
 
 def expert_ffn_is_fused(shape: MoeShape) -> bool:
-    """Whether moe_expert_ffn runs as one persistent launch for this shape (the rule stated in moe.h)."""
-    min_kt = 6 if shape.block_m < 32 else 4
-    two_i, h = 2 * shape.intermediate, shape.hidden
-    return (two_i % 512 == 0 and h % 512 == 0 and two_i // 512 <= 64 and h // 128 >= min_kt
-            and shape.intermediate // 128 >= min_kt)
+    """Whether moe_expert_ffn runs as one persistent launch for this shape."""
+    return gemm_launches(shape)[0] == 1
 
 
 def forward_uses_expert_ffn(shape: MoeShape) -> bool:
-    """Whether moe_forward runs the GEMMs through moe_expert_ffn (block_m < 128) or as moe_linear1 +
-    moe_linear2 (the rule stated in moe.h)."""
-    return shape.block_m < 128
+    """Whether moe_forward runs the GEMMs as one moe_expert_ffn launch (else moe_linear1 + moe_linear2)."""
+    return gemm_launches(shape)[1] == 1
 
 
 def combine(shape: MoeShape, plan_ws, ws, y, stream=None) -> None:

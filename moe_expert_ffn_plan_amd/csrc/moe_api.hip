@@ -84,6 +84,32 @@ int moe_capacity_rows(const moe_shape* shape, int64_t* rows) {
     return MOE_OK;
 }
 
+int moe_suggest_block_m(int64_t num_tokens, int32_t topk, int32_t num_experts, int32_t* block_m) {
+    if (!block_m) return MOE_ERR_NULL;
+    if (num_tokens < 0 || num_tokens >= (1ll << 40) || topk < 1 || topk > kMaxTopk || num_experts < 1)
+        return MOE_ERR_SHAPE;
+    // target rows = imbalance factor 2 x expected rows per expert (T * k / E); the smallest routing
+    // block that holds the target, compared exactly in integers: 2 T k <= c E
+    const int64_t twice_hits = 2 * num_tokens * topk;
+    int32_t pick = 128;
+    for (const int32_t c : {16, 32, 64, 128})
+        if (twice_hits <= (int64_t)c * num_experts) {
+            pick = c;
+            break;
+        }
+    *block_m = pick;
+    return MOE_OK;
+}
+
+int moe_gemm_launches(const moe_shape* shape, int32_t* expert_ffn, int32_t* forward) {
+    if (!expert_ffn || !forward) return MOE_ERR_NULL;
+    const int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    *expert_ffn = fused_supported(*shape) ? 1 : 2;
+    *forward = forward_one_launch(*shape, cu_count()) ? 1 : 2;
+    return MOE_OK;
+}
+
 int moe_plan_workspace_bytes(const moe_shape* shape, size_t* bytes) {
     if (!bytes) return MOE_ERR_NULL;
     const int st = check_shape(shape);
@@ -261,9 +287,7 @@ int moe_forward(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, c
                                           static_cast<hipStream_t>(stream));
         if (e != hipSuccess) return MOE_ERR_HIP;
     }
-    // one persistent launch for small routing blocks (few tiles per CU, where the second launch's ramp
-    // and the first one's tail show), two launches otherwise
-    if (shape->block_m < 128) {
+    if (forward_one_launch(*shape, cu_count())) {
         if ((st = moe_expert_ffn(shape, x, x_sf, topk_w, w1, w1_sf, w2, w2_sf, plan, ws, ws_bytes, stream)) != MOE_OK)
             return st;
     } else {

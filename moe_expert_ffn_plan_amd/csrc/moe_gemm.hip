@@ -495,10 +495,10 @@ __device__ __forceinline__ void epilogue_linear2(const v4f (&acc)[MI][NI], const
         for (int i = 0; i < 4; ++i) {
             const int row_local = wrow0 + mi * 16 + 4 * (lane >> 4) + i;
             if ((PARTIAL && row_local >= rows) || row_tok[row_local] < 0) continue;  // padding rows are never read
-            // 32-bit byte offsets from a uniform base (cap * H * 2 < 2^32)
-            const uint32_t off = ((uint32_t)(m0 + row_local) * (uint32_t)g.N +
-                                  (uint32_t)(gcol0 + 4 * (lane & 15))) * 2u;
-            uint8_t* out = reinterpret_cast<uint8_t*>(g.out_bf16);
+            // the tile's first row is added to the base in 64 bits (uniform: cap * H * 2 may pass 2^32),
+            // the lane's offset inside the tile in 32 bits
+            const uint32_t off = ((uint32_t)row_local * (uint32_t)g.N + (uint32_t)(gcol0 + 4 * (lane & 15))) * 2u;
+            uint8_t* out = reinterpret_cast<uint8_t*>(g.out_bf16) + (size_t)(uint32_t)m0 * (uint32_t)g.N * 2u;
 #pragma unroll
             for (int grp = 0; grp < NI / 4; ++grp) {
                 const uint32_t lo = pack_bf16(acc[mi][grp * 4 + 0][i], acc[mi][grp * 4 + 1][i]);
@@ -954,7 +954,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fused_kernel(FusedArgs fa) {
 }
 
 // Compute units of the current device (cached per device).
-int cu_count() {
+int device_cus() {
     static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -976,7 +976,7 @@ int min_kt_persistent(int bmg) {
 }
 
 int64_t persistent_grid(int64_t all) {
-    const int64_t cus = cu_count() / kNumXcd * kNumXcd;  // one workgroup per CU
+    const int64_t cus = device_cus() / kNumXcd * kNumXcd;  // one workgroup per CU
     return std::max<int64_t>(kNumXcd, std::min(all, cus));
 }
 
@@ -1097,6 +1097,16 @@ bool fused_supported(const moe_shape& s) {
     const int N1 = 2 * s.intermediate, N2 = s.hidden;
     return gemm_bn(N1) == 512 && gemm_bn(N2) == 512 && N1 / 512 <= 64 &&
            s.hidden / kBK >= min_kt_persistent(bmg) && s.intermediate / kBK >= min_kt_persistent(bmg);
+}
+
+int cu_count() { return device_cus(); }
+
+bool forward_one_launch(const moe_shape& s, int cus) {
+    if (!fused_supported(s)) return false;
+    // M-tiles: each expert's padded rows in tiles of bmg, at most cap / bmg + one partial tile per expert
+    const int64_t m_tiles = capacity_rows(s) / gemm_bm(s.block_m) + s.num_experts;
+    const int64_t tiles1 = m_tiles * (2 * s.intermediate / 512);
+    return tiles1 <= (int64_t)kOneLaunchTilesPerCu * cus;
 }
 
 hipError_t launch_expert_ffn(const GemmProblem& p, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,

@@ -136,6 +136,13 @@ hipError_t launch_linear2(const GemmProblem& g, const uint8_t* h_q, const uint8_
 // launches above.  flags: one word per Linear1 tile, any initial contents; status: set to 1 if a
 // Linear2 tile stopped waiting for its rows (never cleared here).
 bool fused_supported(const moe_shape& s);
+// moe_forward runs both GEMMs as that one launch while Linear1 has at most kOneLaunchTilesPerCu tiles
+// per CU in the worst case (every hit local), else as two launches: the single launch hides the
+// first launch's tail and the second one's ramp, which matter only while there are few tiles per CU,
+// and its per-tile cost is a little higher (device-coherent stores, flag polls).
+constexpr int kOneLaunchTilesPerCu = 16;
+bool forward_one_launch(const moe_shape& s, int cus);
+int cu_count();  // compute units of the current device (256 if it cannot be queried)
 hipError_t launch_expert_ffn(const GemmProblem& g, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
                              const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf,
                              const uint8_t* w2, const uint8_t* w2_sf, uint16_t* yslot, uint32_t* flags,

@@ -20,6 +20,11 @@ Workloads (one GPU's share each; expert ids are global, experts
 * ``skewed``   as decode with 16384 tokens, experts drawn Zipf(s=1.2) over
   256 ranks without replacement (Gumbel-top-k), expert id = rank - 1; 10% of
   tokens have x scaled by 50 before quantisation; block_m 128.
+* ``dsv4``     one rank's share of the DeepSeek-V4 expert shape the reading
+  notes' tests use: 8 ranks x 8192 tokens = 65536 tokens routed, hidden
+  7168, intermediate 3072, 48 local of 384 experts, top-6 distinct uniform,
+  Dirichlet(1) weights; block_m 128 (the pages' 192 is not a supported
+  block; 128 is what the block heuristic picks for this shape).
 
 Values: x ~ N(0, 1); weights ~ N(0, std = 1/sqrt(K)) with K the reduction
 size of that GEMM.  Both are quantised per 32 consecutive K elements with a
@@ -60,8 +65,9 @@ WORKLOADS = {
     "prefill": Workload("prefill", 4096, 7168, 2048, 32, 256, 8, 32, "uniform", seed=1003, weight_seed=2002),
     "skewed": Workload("skewed", 16384, 7168, 2048, 32, 256, 8, 128, "zipf", 0.1, 50.0, seed=1004,
                        weight_seed=2002),
+    "dsv4": Workload("dsv4", 65536, 7168, 3072, 48, 384, 6, 128, "uniform", seed=1005, weight_seed=2005),
 }
-ORDER = ["tiny", "tp_slice", "decode", "prefill", "skewed"]
+ORDER = ["tiny", "tp_slice", "decode", "prefill", "skewed", "dsv4"]
 
 
 def _pow2_scale_exponent(amax: torch.Tensor, fmt_max_mant: float, fmt_max_exp: int) -> torch.Tensor:

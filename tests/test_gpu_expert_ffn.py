@@ -7,7 +7,9 @@ which runs the fused launch, is checked against the oracle in
 test_gpu_forward.py).  The cases cover every kernel variant of the fused
 launch (M-tile 16, 128 over whole blocks, 128 over 32-row blocks), a shape
 that falls back to two launches, repeated launches on one workspace (flags
-left by the previous launch) and a second routing on the same workspace.
+left by the previous launch), a second routing on the same workspace and the
+full-size workloads (the DeepSeek-V4 shape included, which moe_forward runs as
+two launches but moe_expert_ffn runs as one).
 """
 import pytest
 import torch
@@ -100,7 +102,7 @@ def test_expert_ffn_new_routing_same_workspace(gpu):
     assert int(B.forward_view(s, ws)["sync_status"].item()) == 0
 
 
-@pytest.mark.parametrize("name", ["tp_slice", "decode", "prefill"])
+@pytest.mark.parametrize("name", ["tp_slice", "decode", "prefill", "dsv4"])
 def test_expert_ffn_full_size_matches_staged(gpu, name):
     w = inputs.WORKLOADS[name]
     assert runs_fused(w)

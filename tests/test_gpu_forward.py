@@ -163,7 +163,7 @@ def test_prepare_weights_layout(gpu, which):
     assert np.array_equal(sft.cpu().numpy(), want_sf)
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill", "skewed"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "skewed", "dsv4"])
 def test_forward_large_sampled(gpu, name):
     w = inputs.WORKLOADS[name]
     print(f"forward parity: {name} full size, sampled tokens", flush=True)

@@ -74,3 +74,80 @@ def test_misaligned_and_small_workspace():
     need = B.plan_workspace_bytes(s)
     assert lib.moe_plan(ctypes.byref(s), ctypes.c_void_p(0x1004), ctypes.c_void_p(0x10000), need, None) == -3
     assert lib.moe_plan(ctypes.byref(s), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x10000), need - 1, None) == -4
+
+
+# Routing block heuristic (walk-through section 7.1, "BLOCK_M selection"): target = 2 (imbalance
+# factor) x expected rows per expert, expected = tokens x topk / experts; the smallest supported block
+# (16, 32, 64, 128) that holds the target, else 128.  Each case states its target.
+@pytest.mark.parametrize("T,k,E,want", [
+    (128, 8, 256, 16),     # decode: expected 4, target 8
+    (256, 8, 256, 16),     # target exactly 16: equality keeps the smaller block
+    (257, 8, 256, 32),     # target 16.06
+    (512, 8, 256, 32),     # target 32
+    (1024, 8, 256, 64),    # target 64
+    (1025, 8, 256, 128),   # target 64.06
+    (2048, 8, 256, 128),   # target 128
+    (4096, 8, 256, 128),   # prefill: target 256, above the ladder
+    (2048, 8, 64, 128),    # TP slice: target 512
+    (8 * 8192, 6, 384, 128),  # DeepSeek-V4 test shape, 8 ranks x 8192 tokens, top-6 of 384: target 2048
+    (64, 2, 8, 32),        # tiny: expected 16, target 32
+    (0, 8, 256, 16),       # no tokens: the smallest block
+    (1, 1, 1, 16),         # target 2
+])
+def test_suggest_block_m_table(T, k, E, want):
+    assert B.suggest_block_m(T, k, E) == want
+
+
+def test_suggest_block_m_ladder_properties():
+    prev = 16
+    for T in range(0, 5000, 7):
+        bm = B.suggest_block_m(T, 8, 256)
+        assert bm in (16, 32, 64, 128) and bm >= prev  # one of the blocks, never smaller with more tokens
+        target = 2 * T * 8 / 256
+        assert bm >= target or bm == 128
+        assert bm == 16 or bm // 2 < target  # the smallest block that holds the target
+        prev = bm
+
+
+@pytest.mark.parametrize("args,status", [((-1, 8, 256), -2), ((16, 0, 256), -2), ((16, 65, 256), -2),
+                                         ((16, 8, 0), -2), ((1 << 40, 8, 256), -2)])
+def test_suggest_block_m_rejects(args, status):
+    v = ctypes.c_int32()
+    assert B.lib().moe_suggest_block_m(*args, ctypes.byref(v)) == status
+    assert B.lib().moe_suggest_block_m(16, 8, 256, None) == -1
+
+
+def _launch_rule(T, H, I, E, k, bm, cus=256):
+    """moe_forward's rule as moe.h states it: one launch when moe_expert_ffn supports it and the worst-case
+    Linear1 tile count (cap / M + E) * (2I / 512) is at most 16 per compute unit."""
+    M = 16 if bm == 16 else 128
+    min_kt = 6 if bm == 16 else 4
+    fused = (2 * I) % 512 == 0 and H % 512 == 0 and 2 * I // 512 <= 64 and H // 128 >= min_kt and I // 128 >= min_kt
+    tiles = (capacity_rows(T, k, E, bm) // M + E) * (2 * I // 512)
+    return (1 if fused else 2), (1 if fused and tiles <= 16 * cus else 2)
+
+
+@pytest.mark.parametrize("T,H,I,E,k,bm", [
+    (2048, 4096, 768, 64, 8, 128), (128, 7168, 2048, 32, 8, 16), (4096, 7168, 2048, 32, 8, 32),
+    (16384, 7168, 2048, 32, 8, 128), (64, 256, 128, 8, 2, 128), (400, 1024, 256, 5, 3, 64),
+    (300, 1024, 768, 10, 6, 16), (65536, 7168, 3072, 48, 6, 128), (4096, 7168, 2048, 32, 8, 128),
+    (8192, 7168, 2048, 32, 8, 32), (100, 7168, 2048, 32, 8, 16)])
+def test_gemm_launches_rule(T, H, I, E, k, bm):
+    s = B.make_shape(T, H, I, E, k, bm)
+    cus = 256
+    try:
+        import torch
+        if torch.cuda.is_available():
+            cus = torch.cuda.get_device_properties(0).multi_processor_count
+    except Exception:
+        pass
+    assert B.gemm_launches(s) == _launch_rule(T, H, I, E, k, bm, cus)
+
+
+def test_gemm_launches_named_workloads():
+    # the configurations the measurements cover: one launch except for the two large batches (and the
+    # tiny shape, whose 2I = 256 is not a multiple of 512)
+    from moe_expert_ffn_plan_amd import inputs
+    got = {n: B.gemm_launches(B.shape_of(w)) for n, w in inputs.WORKLOADS.items()}
+    assert got["tiny"] == (2, 2) and got["decode"] == (1, 1) and got["prefill"] == (1, 1)
+    assert got["tp_slice"] == (1, 1) and got["skewed"] == (1, 2) and got["dsv4"] == (1, 2)
