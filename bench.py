@@ -7,8 +7,8 @@ One step = the whole hot path on one batch of synthetic input already resident
 in HBM: routing tables (moe_plan), grouped Linear1 with the fused
 SwiGLU/requant epilogue, grouped Linear2, and the top-k combine, enqueued on
 one stream.  The stages are the calls moe_forward makes (moe_plan,
-moe_expert_ffn, both GEMMs in one persistent launch, for block_m < 128, else
-moe_linear1 and moe_linear2; moe_combine); they are issued one by one so HIP
+moe_expert_ffn, both GEMMs in one persistent launch, or moe_linear1 and
+moe_linear2, as moe_gemm_launches reports; moe_combine); they are issued one by one so HIP
 events on that stream can bracket the dominant GEMM launch inside the timed
 steps (the roofline's achieved rate).  --staged and --expert-ffn force one
 schedule or the other.  Three copies of the
@@ -18,7 +18,9 @@ settle; the first steps after idle run ~15% slower.
 
 Prints one JSON line with the metric (useful TFLOP/s = 2 * N_valid * 3 * H * I
 per step, the reading notes' FLOP count, over the wall time of the timed
-steps), tokens/s, the roofline of the dominant kernel, per-stage kernel times
+steps), tokens/s, the share of the step's compulsory HBM bytes per second in
+the HBM peak, the roofline of the dominant kernel (MFMA or HBM, whichever
+bounds its algorithmic work), per-stage kernel times
 from a separate untimed pass with an event between every stage, and the CPU
 oracle timed on a bounded sample of the same workload.
 """
@@ -57,6 +59,20 @@ def kernel_traffic(kind: str, workload: str):
     if fields.get("kernel_source_sha256") != digest or fields.get("workload") != workload:
         return None
     return int(fields["traffic_bytes_per_launch"])
+
+
+def kernel_bytes(w, fused: bool, n_valid: int, touched: int, hit_tokens: int) -> int:
+    """Algorithmic HBM bytes of one launch of the dominant GEMM kernel: what it must read and write once.
+    Linear1: W1 and its scales for every expert with a row, x and x_sf of every token with a local hit,
+    one top-k weight per row, h_q and h_sf written.  Both GEMMs in one launch: that, plus W2 and its
+    scales for the same experts, h_q and h_sf read back, and the BF16 yslot rows written."""
+    H, I = w.hidden, w.intermediate
+    w1 = touched * 2 * I * H * (1 / 2 + 1 / 32)
+    h = n_valid * I * (1 + 1 / 32)
+    b = w1 + hit_tokens * H * (1 + 1 / 32) + n_valid * 4 + h
+    if fused:
+        b += touched * H * I * (1 / 2 + 1 / 32) + h + n_valid * H * 2
+    return int(b)
 
 
 def cpu_baseline(w, d_gpu, sample_tokens: int, min_seconds: float = 10.0):
@@ -151,8 +167,8 @@ def main() -> int:
     ws = torch.empty(B.forward_workspace_bytes(s), dtype=torch.uint8, device=dev)
     y = torch.empty(w.num_tokens, w.hidden, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
-    # the schedule moe_forward picks: moe_expert_ffn (one persistent launch where the shape allows) for
-    # block_m < 128, else the two GEMM launches
+    # the schedule moe_forward picks (moe_gemm_launches): one persistent launch for both GEMMs while
+    # Linear1 has few tiles per CU, else the two GEMM launches
     fused = B.forward_uses_expert_ffn(s) and B.expert_ffn_is_fused(s) and not args.staged
     if args.expert_ffn:
         fused = B.expert_ffn_is_fused(s)
@@ -185,8 +201,12 @@ def main() -> int:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    scal = B.plan_view(s, plan_ws)["scalars"].cpu().tolist()
+    pv = B.plan_view(s, plan_ws)
+    scal = pv["scalars"].cpu().tolist()
     r_pad, n_valid = scal[0], scal[2]
+    touched = int((pv["counts"] > 0).sum().item())  # experts with at least one row
+    ids = d["topk_idx"]
+    hit_tokens = int(((ids >= 0) & (ids < w.num_experts)).any(dim=1).sum().item())
 
     # timed steps: wall time; HIP events bracket only the dominant GEMM launch (same stream)
     k_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
@@ -223,9 +243,18 @@ def main() -> int:
         k_flops = 2.0 * n_valid * 2 * I * H
         kname = "Linear1 grouped GEMM (%s<%d, true, %s, 0>)" % (
             "gemm_pp_kernel" if (2 * I) % 512 == 0 else "gemm4_kernel", bmg, partial)
-    k_tflops = k_flops / (k_ms * 1e-3) / 1e12
-    roofline = {"kernel": kname, "bound": "mfma", "achieved": round(k_tflops, 2),
-                "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_MFMA_TFLOPS, 4),
+    k_bytes = kernel_bytes(w, fused, n_valid, touched, hit_tokens)
+    # whole step, compulsory: touched weights and scales, x and x_sf of tokens with a local hit, the
+    # top-k ids and weights, y
+    step_bytes = int(touched * 3 * I * H * (1 / 2 + 1 / 32) + hit_tokens * H * (1 + 1 / 32) +
+                     w.num_tokens * w.topk * 12 + w.num_tokens * H * 2)
+    # the roofline that bounds the kernel: the larger of its MFMA time and its HBM time at peak
+    if k_bytes / (PEAK_HBM_GBS * 1e9) > k_flops / (PEAK_MFMA_TFLOPS * 1e12):
+        achieved, peak, unit, bound = k_bytes / (k_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    else:
+        achieved, peak, unit, bound = k_flops / (k_ms * 1e-3) / 1e12, PEAK_MFMA_TFLOPS, "TFLOP/s", "mfma"
+    roofline = {"kernel": kname, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "algorithmic_flops": k_flops, "algorithmic_bytes": k_bytes,
                 "traffic": kernel_traffic("expert_ffn" if fused else "linear1", w.name)}
     out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
@@ -235,6 +264,8 @@ def main() -> int:
                       "valid_rows": n_valid, "padded_rows": r_pad, "weight_copies": args.weight_copies},
            "tokens_per_s": round(w.num_tokens / (ms * 1e-3), 1),
            "pct_of_mfma_peak": round(100 * tflops / PEAK_MFMA_TFLOPS, 2),
+           "pct_of_hbm_peak": round(100 * step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+           "step_algorithmic_bytes": step_bytes,
            "gemm_ms": round(k_ms, 4),
            "kernel_ms": {k: round(v, 4) for k, v in kern_ms.items()},
            "roofline": roofline}
