@@ -16,6 +16,14 @@
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    outputs are valid once the stream reaches the call.  No call blocks on
  *    the GPU.  Calls that share a workspace must not overlap in time.
+ *  - Stream capture: no call allocates, synchronizes or enqueues a memset,
+ *    so the enqueueing calls can be recorded into a HIP graph and the graph
+ *    replayed (the practice page rebuilds its schedule tables from a
+ *    captured graph and allocates every buffer once for that reason,
+ *    sections 2 and 5);
+ *    replays are calls like any other and must not overlap on one
+ *    workspace.  Call once eagerly before capturing (the first call on a
+ *    device queries its properties).
  *  - Validation happens on the host before anything is enqueued, in this
  *    order: NULL shape/pointers (MOE_ERR_NULL), shape limits (MOE_ERR_SHAPE),
  *    alignment (MOE_ERR_ALIGN), workspace size (MOE_ERR_WORKSPACE), device
@@ -264,7 +272,9 @@ MOE_API int moe_combine(const moe_shape* shape, const void* plan_ws,
  * them with a fresh epoch); calls sharing a ws must not overlap.  A Linear2
  * tile that waits for about half a second gives up and sets the forward view's
  * sync_status to 1 (it needs every workgroup of the launch resident at once;
- * the library never clears the word). */
+ * the library never clears the word).  When `stream` is being captured, a
+ * one-thread kernel that advances an epoch word in ws is recorded ahead of
+ * the launch, so every replay of the graph stamps fresh flags. */
 MOE_API int moe_expert_ffn(const moe_shape* shape,
                 const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
                 const uint8_t* w1, const uint8_t* w1_sf,

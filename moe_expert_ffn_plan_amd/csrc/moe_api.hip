@@ -244,7 +244,7 @@ int moe_expert_ffn(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf
         g, x, x_sf, topk_w, w1, w1_sf, reinterpret_cast<uint8_t*>(base + F.h_q),
         reinterpret_cast<uint8_t*>(base + F.h_sf), w2, w2_sf, reinterpret_cast<uint16_t*>(base + F.yslot),
         reinterpret_cast<uint32_t*>(base + F.flags), reinterpret_cast<uint32_t*>(base + F.status),
-        static_cast<hipStream_t>(stream));
+        reinterpret_cast<uint32_t*>(base + F.epoch), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

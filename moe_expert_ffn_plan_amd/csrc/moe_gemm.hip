@@ -919,7 +919,19 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
 struct FusedArgs {
     GemmArgs g1, g2;  // Linear1, Linear2
     FusedSync sync;
+    // launches recorded into a graph: a word the preceding epoch_bump_kernel advanced, mixed into
+    // sync.epoch (whose host value is frozen at capture) so that each replay stamps fresh flags
+    const uint32_t* epoch_word;
 };
+
+// Advances the device epoch word of a forward workspace (one thread; runs before every recorded
+// single-launch GEMM).
+__global__ void epoch_bump_kernel(uint32_t* word) {
+    if (threadIdx.x == 0) {
+        const uint32_t v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(word, v + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
 
 // Linear1 then Linear2 in one launch.  Each XCD runs the Linear1 and then the Linear2 tiles of its
 // M-tiles.  Its Linear1 tiles go round-robin to its workgroups, so the first r1 slots run one tile
@@ -931,11 +943,16 @@ template <int BM, bool PARTIAL, int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_fused_kernel(FusedArgs fa) {
     __shared__ PPShared<BM> sh;
     const int nslots = gridDim.x / kNumXcd, xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+    FusedSync sync = fa.sync;
+    if (fa.epoch_word) {  // every workgroup reads the same value: nothing in this launch writes the word
+        const uint32_t e = sync.epoch ^ __hip_atomic_load(fa.epoch_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sync.epoch = __builtin_amdgcn_readfirstlane(e != 0u ? e : 0x9E3779B9u);
+    }
     int b1, e1, b2, e2;
     xcd_chunk(fa.g1, fa.g1.N / 512, xcd, b1, e1);
     xcd_chunk(fa.g2, fa.g2.N / 512, xcd, b2, e2);
     const TileSeq s1 = round_robin(b1, e1, slot, nslots);
-    if (s1.n > 0) pp_run<BM, true, PARTIAL, true, EPI>(fa.g1, fa.sync, s1, sh);
+    if (s1.n > 0) pp_run<BM, true, PARTIAL, true, EPI>(fa.g1, sync, s1, sh);
     wait_and_barrier<0>();  // the Linear1 run's table loads have landed before the tables are reused
 
     const int r1 = (e1 - b1) % nslots, nl = r1 > 0 ? nslots - r1 : 0;  // light workgroups: slots >= r1
@@ -950,7 +967,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fused_kernel(FusedArgs fa) {
     s2.first_b = b2 + na_all + slot;
     s2.stride_b = nslots;
     s2.n = s2.n_a + (s2.first_b < e2 ? (e2 - s2.first_b + nslots - 1) / nslots : 0);
-    if (s2.n > 0) pp_run<BM, false, PARTIAL, true, kEpiFast>(fa.g2, fa.sync, s2, sh);
+    if (s2.n > 0) pp_run<BM, false, PARTIAL, true, kEpiFast>(fa.g2, sync, s2, sh);
 }
 
 // Compute units of the current device (cached per device).
@@ -1112,7 +1129,7 @@ bool forward_one_launch(const moe_shape& s, int cus) {
 hipError_t launch_expert_ffn(const GemmProblem& p, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
                              const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf,
                              const uint8_t* w2, const uint8_t* w2_sf, uint16_t* yslot, uint32_t* flags,
-                             uint32_t* status, hipStream_t stream) {
+                             uint32_t* status, uint32_t* epoch_word, hipStream_t stream) {
     FusedArgs fa{};
     fa.g1 = linear1_args(p, x, x_sf, topk_w, w1, w1_sf, h_q, h_sf);
     fa.g2 = linear2_args(p, h_q, h_sf, w2, w2_sf, yslot);
@@ -1130,6 +1147,14 @@ hipError_t launch_expert_ffn(const GemmProblem& p, const uint8_t* x, const uint8
     const dim3 grid((unsigned)persistent_grid(tiles)), block(512);
     const int bm = p.shape->block_m, bmg = gemm_bm(bm);
     const int epi = epi_of(fa.g1);
+    // a launch being recorded into a graph would replay the host epoch above: advance a device word first
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive) {
+        hipLaunchKernelGGL(epoch_bump_kernel, dim3(1), dim3(64), 0, stream, epoch_word);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        fa.epoch_word = epoch_word;
+    }
     if (bmg == 16) launch_fused<16, false>(epi, grid, block, stream, fa);
     else if (bm == 128) launch_fused<128, false>(epi, grid, block, stream, fa);
     else launch_fused<128, true>(epi, grid, block, stream, fa);

@@ -82,7 +82,7 @@ inline PlanLayout plan_layout(const moe_shape& s) {
 // Offsets (bytes) inside a forward workspace: the plan region first.
 struct ForwardLayout {
     PlanLayout plan;
-    size_t plan_base = 0, h_q = 0, h_sf = 0, yslot = 0, flags = 0, status = 0, total = 0;
+    size_t plan_base = 0, h_q = 0, h_sf = 0, yslot = 0, flags = 0, status = 0, epoch = 0, total = 0;
 };
 
 inline ForwardLayout forward_layout(const moe_shape& s) {
@@ -96,6 +96,7 @@ inline ForwardLayout forward_layout(const moe_shape& s) {
     F.yslot = take((size_t)F.plan.cap * s.hidden * 2);
     F.flags = take((size_t)F.plan.max_tiles1 * 4);  // one word per Linear1 tile (fused launch)
     F.status = take(4);
+    F.epoch = take(4);  // advanced by single launches recorded into a graph
     F.total = o;
     return F;
 }
@@ -134,7 +135,8 @@ hipError_t launch_linear2(const GemmProblem& g, const uint8_t* h_q, const uint8_
                           const uint8_t* w2_sf, uint16_t* yslot, hipStream_t stream);
 // Both GEMMs in one persistent launch when the shape allows it (fused_supported), else the two
 // launches above.  flags: one word per Linear1 tile, any initial contents; status: set to 1 if a
-// Linear2 tile stopped waiting for its rows (never cleared here).
+// Linear2 tile stopped waiting for its rows (never cleared here); epoch_word: any initial contents,
+// advanced by a one-thread kernel ahead of the launch when the stream is being captured.
 bool fused_supported(const moe_shape& s);
 // moe_forward runs both GEMMs as that one launch while Linear1 has at most kOneLaunchTilesPerCu tiles
 // per CU in the worst case (every hit local), else as two launches: the single launch hides the
@@ -146,7 +148,7 @@ int cu_count();  // compute units of the current device (256 if it cannot be que
 hipError_t launch_expert_ffn(const GemmProblem& g, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
                              const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf,
                              const uint8_t* w2, const uint8_t* w2_sf, uint16_t* yslot, uint32_t* flags,
-                             uint32_t* status, hipStream_t stream);
+                             uint32_t* status, uint32_t* epoch_word, hipStream_t stream);
 hipError_t launch_tile_weights(int which, int N, int K, int E, const uint8_t* w, const uint8_t* w_sf,
                                uint8_t* w_out, uint8_t* sf_out, hipStream_t stream);
 hipError_t launch_combine(const moe_shape& s, const uint16_t* yslot, const int32_t* slot, uint16_t* y,

@@ -1,0 +1,86 @@
+"""GPU tests of stream capture: moe_plan + moe_forward recorded into a HIP graph and replayed.
+
+The practice page rebuilds its schedule tables with a captured graph and keeps every buffer
+allocated once so that the layer can be replayed (sections 2 and 5).  Here the whole forward is
+recorded once; each replay runs on new inputs copied into the captured buffers, and its output
+must equal an eager moe_forward on the same inputs bit for bit.  Eager work and synchronisation
+run between the replays.  The single-launch GEMM stamps its completion flags with an epoch
+that a recorded one-thread kernel advances on every replay; a replay that reused the previous
+replay's epoch would find its flags already set and could read rows Linear1 has not yet written.
+"""
+import pytest
+import torch
+
+from moe_expert_ffn_plan_amd import binding as B
+from moe_expert_ffn_plan_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # one persistent launch for both GEMMs (128-row tiles over 32-row blocks)
+    "one_launch": inputs.Workload("graph_one_launch", 700, 1024, 512, 7, 9, 5, 32, "uniform", seed=61,
+                                  weight_seed=71),
+    # 16-row tiles, one launch
+    "one_launch_bm16": inputs.Workload("graph_bm16", 300, 1024, 768, 6, 10, 4, 16, "uniform", seed=62,
+                                       weight_seed=72),
+    # I = 256: the GEMMs run as two launches
+    "two_launches": inputs.Workload("graph_two", 400, 1024, 256, 5, 5, 3, 64, "uniform", seed=63, weight_seed=73),
+}
+
+
+def _eager(s, d, dev):
+    y = torch.empty(d["x"].shape[0], s.hidden, dtype=torch.bfloat16, device=dev)
+    ws = torch.full((B.forward_workspace_bytes(s),), 0x5A, dtype=torch.uint8, device=dev)
+    plan_ws = torch.empty(B.plan_workspace_bytes(s), dtype=torch.uint8, device=dev)
+    B.plan(s, d["topk_idx"], plan_ws)
+    B.forward(s, d["x"], d["x_sf"], d["topk_idx"], d["topk_w"], d["w1"], d["w1_sf"], d["w2"], d["w2_sf"], y, ws,
+              plan_ws=plan_ws)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_forward_graph_replays(gpu, name):
+    w = CASES[name]
+    s = B.shape_of(w)
+    print(f"graph replay: {name} T={w.num_tokens} bm={w.block_m} launches={B.gemm_launches(s)}", flush=True)
+    weights = {k: v.to(gpu) for k, v in inputs.make_weights(w, device="cpu").items()}
+    weights.update(B.prepare_all(s, weights))
+
+    def draw(seed):
+        d = {k: v.to(gpu) for k, v in inputs.make_inputs(w, device="cpu", seed=seed, with_weights=False).items()}
+        d.update(weights)
+        return d
+
+    static = draw(100)
+    y = torch.empty(w.num_tokens, w.hidden, dtype=torch.bfloat16, device=gpu)
+    ws = torch.full((B.forward_workspace_bytes(s),), 0x5A, dtype=torch.uint8, device=gpu)
+    plan_ws = torch.empty(B.plan_workspace_bytes(s), dtype=torch.uint8, device=gpu)
+    status = B.forward_view(s, ws)["sync_status"]
+    status.zero_()
+
+    def run():
+        B.plan(s, static["topk_idx"], plan_ws)
+        B.forward(s, static["x"], static["x_sf"], static["topk_idx"], static["topk_w"], static["w1"],
+                  static["w1_sf"], static["w2"], static["w2_sf"], y, ws, plan_ws=plan_ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()  # eager call before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    torch.cuda.synchronize()
+    for rep, seed in enumerate((101, 102, 103, 101)):
+        new = draw(seed)
+        for key in ("x", "x_sf", "topk_idx", "topk_w"):
+            static[key].copy_(new[key])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        want = _eager(s, new, gpu)  # eager work between replays
+        assert torch.equal(y.view(torch.int16), want.view(torch.int16)), f"{name}: replay {rep} differs from eager"
+    assert int(status.item()) == 0, "a Linear2 tile gave up waiting"
