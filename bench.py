@@ -116,6 +116,8 @@ def main() -> int:
                     help="run Linear1 and Linear2 through moe_expert_ffn (one launch) wherever it is supported")
     ap.add_argument("--host-inputs", action="store_true",
                     help="draw the synthetic inputs on the CPU and copy them (fewer torch GPU kernels, for profilers)")
+    ap.add_argument("--graph", action="store_true",
+                    help="record each step (one per weight copy) into a HIP graph and time graph replays")
     ap.add_argument("--block-m", type=int, default=0,
                     help="routing block rows to use instead of the workload's own (16, 32, 64 or 128)")
     ap.add_argument("--tokens", type=int, default=0,
@@ -177,6 +179,7 @@ def main() -> int:
     def step(i, events=None, k_events=None, staged=not fused):
         """One step; events: one per stage boundary; k_events: around the dominant GEMM launch."""
         wt = weights[i % len(weights)]
+        stream = torch.cuda.current_stream()  # the capture stream while a graph is being recorded
         rec = (lambda j: events[j].record(stream)) if events is not None else (lambda j: None)
         rec(0)
         B.plan(s, d["topk_idx"], plan_ws, stream)
@@ -210,12 +213,36 @@ def main() -> int:
 
     # timed steps: wall time; HIP events bracket only the dominant GEMM launch (same stream)
     k_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, k_events=k_evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    if args.graph:
+        # one recorded step per weight copy; the timed loop replays them in turn, and the events around
+        # the dominant launch come from an eager pass right after
+        graphs = []
+        side = torch.cuda.Stream()
+        for c in range(len(weights)):
+            side.wait_stream(torch.cuda.current_stream())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                step(c)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(len(graphs) * 4):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, k_events=k_evs[i])
+        torch.cuda.synchronize()
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, k_events=k_evs[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
     k_ms = sum(e[0].elapsed_time(e[1]) for e in k_evs) / args.steps
 
@@ -261,7 +288,8 @@ def main() -> int:
            "vs_baseline": None, "dtype": "fp8e4m3 x fp4e2m1 (fp32 accumulate)", "data": "synthetic",
            "config": {"workload": w.name, "tokens": w.num_tokens, "hidden": H, "intermediate": I,
                       "local_experts": w.num_experts, "topk": w.topk, "block_m": w.block_m,
-                      "valid_rows": n_valid, "padded_rows": r_pad, "weight_copies": args.weight_copies},
+                      "valid_rows": n_valid, "padded_rows": r_pad, "weight_copies": args.weight_copies,
+                      "launch": "graph" if args.graph else "stream"},
            "tokens_per_s": round(w.num_tokens / (ms * 1e-3), 1),
            "pct_of_mfma_peak": round(100 * tflops / PEAK_MFMA_TFLOPS, 2),
            "pct_of_hbm_peak": round(100 * step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),

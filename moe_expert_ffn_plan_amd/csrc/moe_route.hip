@@ -36,6 +36,35 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 
+// Workgroup barrier for LDS traffic only.  Apart from route_scan_kernel, these kernels never read global
+// memory that another thread of the same launch wrote, so their barriers need not wait for outstanding
+// global stores the way __syncthreads does (a round trip to memory per barrier, after every pass that
+// writes tables).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wave-level inclusive scans with DPP lane moves (a few cycles each; a __shfl_up goes through the LDS
+// crossbar at LDS latency).  Lanes whose source lies outside the row read 0.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ int dpp_add(int v) {
+    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+// within each row of 16 lanes
+__device__ __forceinline__ int row_inclusive_scan(int v) {
+    v = dpp_add<0x111>(v);  // row_shr:1
+    v = dpp_add<0x112>(v);  // row_shr:2
+    v = dpp_add<0x114>(v);  // row_shr:4
+    return dpp_add<0x118>(v);  // row_shr:8
+}
+// across the 64 lanes: the row scans, then lane 15 of each row into the next row and lane 31 into the
+// upper half
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    v = row_inclusive_scan(v);
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+    return dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+}
+
 __device__ __forceinline__ uint64_t lanes_lt() { return (1ull << (threadIdx.x & 63)) - 1ull; }
 
 // Lanes of this wave whose `valid` key equals mine (only meaningful if valid).
@@ -51,25 +80,62 @@ __device__ __forceinline__ uint64_t match_peers(bool valid, int key, int nbits) 
 
 // Inclusive scan of one value per thread across the workgroup.
 __device__ int block_inclusive_scan(int v, int* scratch) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(v, d, 64);
-        if (lane >= d) v += o;
-    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+    v = wave_inclusive_scan(v);
     if (lane == 63) scratch[wave] = v;
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
-        int t = lane < kWaves ? scratch[lane] : 0;
-        for (int d = 1; d < kWaves; d <<= 1) {
-            const int o = __shfl_up(t, d, 64);
-            if (lane >= d) t += o;
-        }
-        if (lane < kWaves) scratch[lane] = t;
+        const int t = wave_inclusive_scan(lane < waves ? scratch[lane] : 0);
+        if (lane < waves) scratch[lane] = t;
     }
-    __syncthreads();
+    lds_barrier();
     if (wave > 0) v += scratch[wave - 1];
-    __syncthreads();
+    lds_barrier();
     return v;
+}
+
+// Inclusive scans of N values per thread across the workgroup, sharing one set of barriers.
+// scratch: N * 64 ints.
+template <int N>
+__device__ void block_inclusive_scan_n(int (&v)[N], int* scratch) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = wave_inclusive_scan(v[i]);
+    if (lane == 63)
+#pragma unroll
+        for (int i = 0; i < N; ++i) scratch[i * 64 + wave] = v[i];
+    lds_barrier();
+    if (wave == 0)
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int t = wave_inclusive_scan(lane < waves ? scratch[i * 64 + lane] : 0);
+            if (lane < waves) scratch[i * 64 + lane] = t;
+        }
+    lds_barrier();
+    if (wave > 0)
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] += scratch[i * 64 + wave - 1];
+    lds_barrier();
+}
+
+// Per-wave counters cnt[w * E + e] (w < W) turned in place into each wave's exclusive prefix over
+// the waves before it, with totals[e] = the sum over all W waves.  Thread t handles wave t % W of
+// expert t / W (W = 16 lanes per expert: one DPP row scan).  No barrier inside: callers synchronise
+// before and after.
+template <int W>
+__device__ void wave_prefix(int32_t* cnt, int E, int32_t* totals) {
+    static_assert(W == 16, "one DPP row of 16 lanes per expert");
+    const int ww = threadIdx.x & (W - 1);
+    const int per = blockDim.x / W;  // experts per pass
+    for (int e0 = 0; e0 < E; e0 += per) {  // the same trip count for every thread (convergent shuffles)
+        const int e = e0 + (int)threadIdx.x / W;
+        const int c = e < E ? cnt[ww * E + e] : 0;
+        const int v = row_inclusive_scan(c);
+        if (e < E) {
+            cnt[ww * E + e] = v - c;
+            if (ww == W - 1) totals[e] = v;
+        }
+    }
 }
 
 
@@ -93,16 +159,13 @@ __device__ void write_tile_lists(const int32_t* soff, int E, int bm, int32_t* tb
                 const int nb = (soff[e + 1] - soff[e]) / bm;
                 v = (nb + ratio - 1) / ratio;
             }
-            for (int d = 1; d < 64; d <<= 1) {
-                const int o = __shfl_up(v, d, 64);
-                if (lane >= d) v += o;
-            }
+            v = wave_inclusive_scan(v);
             if (e < E) tb[e + 1] = run + v;
-            run += __shfl(v, 63, 64);
+            run += __builtin_amdgcn_readlane(v, 63);
         }
         if (lane == 0) tb[0] = 0;
     }
-    __syncthreads();
+    lds_barrier();
     const int mt_total = tb[E];
     if (counts && threadIdx.x == 0) {
         p.scalars[4] = mt_total * p.nt1;
@@ -143,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
     __shared__ int32_t scnt[kMaxExperts];          // counts (later pull counts)
     __shared__ int32_t sbase[kMaxExperts + 1];     // pull-order bases
     __shared__ int32_t tb[kMaxExperts + 1];        // M-tile bases per expert
-    __shared__ int32_t scratch[64];
+    __shared__ int32_t scratch[128];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     const int64_t begin = expert_begin;
@@ -164,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
         }
     }
     for (int i = tid; i < kWaves * E; i += kThreads) wcnt[i] = 0;
-    __syncthreads();
+    lds_barrier();
 
     // ---- pass 1: hits per (wave, expert); wave w owns the contiguous hits [h0, h1)
     const int per_wave = (nh + kWaves * 64 - 1) / (kWaves * 64) * 64;
@@ -174,23 +237,15 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
         const int e = le[h];
         if (e >= 0) atomicAdd(&wcnt[w * E + e], 1);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- pass 2: per-wave bases, counts, padded offsets
-    for (int e = tid; e < E; e += kThreads) {
-        int run = 0;
-        for (int ww = 0; ww < kWaves; ++ww) {
-            const int c = wcnt[ww * E + e];
-            wcnt[ww * E + e] = run;
-            run += c;
-        }
-        scnt[e] = run;
-    }
-    __syncthreads();
+    wave_prefix<kWaves>(wcnt, E, scnt);
+    lds_barrier();
     const int cnt = tid < E ? scnt[tid] : 0;
-    const int padded = (cnt + bm - 1) / bm * bm;
-    const int incl_pad = block_inclusive_scan(padded, scratch);
-    const int incl_cnt = block_inclusive_scan(cnt, scratch);
+    int sv[2] = {(cnt + bm - 1) / bm * bm, cnt};
+    block_inclusive_scan_n<2>(sv, scratch);
+    const int incl_pad = sv[0], incl_cnt = sv[1];
     if (tid < E) {
         soff[tid + 1] = incl_pad;
         p.counts[tid] = cnt;
@@ -205,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
         p.scalars[2] = incl_cnt;        // N
         p.scalars[3] = incl_pad / bm;   // n_blocks
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- pass 3: stable scatter of hits into rows, 64 at a time in flat order
     for (int base = h0; base < h1; base += 64) {
@@ -247,11 +302,11 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
         }
     }
     write_tile_lists(soff, E, bm, tb, p, 0, 1, true);
-    __syncthreads();
+    lds_barrier();
 
     // ---- pass 5: pull order = tokens with a hit, by smallest local expert, then t
     for (int i = tid; i < kWaves * E; i += kThreads) wcnt[i] = 0;
-    __syncthreads();
+    lds_barrier();
     const int tper = (T + kWaves * 64 - 1) / (kWaves * 64) * 64;
     const int t0 = min(T, w * tper), t1 = min(T, t0 + tper);
     auto smallest = [&](int t) {
@@ -267,23 +322,15 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
         const int emin = t < t1 ? smallest(t) : E;
         if (emin < E) atomicAdd(&wcnt[w * E + emin], 1);
     }
-    __syncthreads();
-    for (int e = tid; e < E; e += kThreads) {
-        int run = 0;
-        for (int ww = 0; ww < kWaves; ++ww) {
-            const int c = wcnt[ww * E + e];
-            wcnt[ww * E + e] = run;
-            run += c;
-        }
-        scnt[e] = run;  // counts are no longer needed; reuse for pull counts
-    }
-    __syncthreads();
+    lds_barrier();
+    wave_prefix<kWaves>(wcnt, E, scnt);  // counts are no longer needed; scnt takes the pull counts
+    lds_barrier();
     const int pc = tid < E ? scnt[tid] : 0;
     const int incl_pull = block_inclusive_scan(pc, scratch);
     if (tid < E) sbase[tid + 1] = incl_pull;
     if (tid == 0) sbase[0] = 0;
     if (tid == E - 1) p.scalars[1] = incl_pull;  // n_pull
-    __syncthreads();
+    lds_barrier();
     for (int base = t0; base < t1; base += 64) {
         const int t = base + lane;
         const int emin = t < t1 ? smallest(t) : E;
@@ -344,7 +391,7 @@ __global__ __launch_bounds__(kGThreads) void route_count_kernel(const int64_t* _
     for (int i = tid; i < 2 * E; i += kGThreads) lds[i] = 0;
     const int t0 = g * kRouteTokensPerGroup, t1 = min(T, t0 + kRouteTokensPerGroup);
     load_group_experts(ids, (int64_t)t0 * k, (int64_t)t1 * k, k, expert_begin, E, le);
-    __syncthreads();
+    lds_barrier();
     const int nh = (t1 - t0) * k;
     for (int i = tid; i < nh; i += kGThreads)
         if (le[i] >= 0) atomicAdd(&ch[le[i]], 1);
@@ -352,7 +399,7 @@ __global__ __launch_bounds__(kGThreads) void route_count_kernel(const int64_t* _
         const int emin = smallest_in(le, t, k, E);
         if (emin < E) atomicAdd(&cp[emin], 1);
     }
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < E; e += kGThreads) {
         gcounts[(size_t)g * E + e] = ch[e];
         gcounts[((size_t)groups + g) * E + e] = cp[e];
@@ -542,8 +589,8 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int
     int32_t* pbase = scnt + E;              // [E+1] pull bases
     int32_t* gh = pbase + E + 1;            // [E] this group's first row of each expert (before soff)
     int32_t* gp = gh + E;                   // [E] this group's first pull position (before pbase)
-    int32_t* scratch = gp + E;              // [64]
-    int32_t* tb = scratch + 64;             // [E+1] M-tile bases
+    int32_t* scratch = gp + E;              // [192]
+    int32_t* tb = scratch + 192;            // [E+1] M-tile bases
     int32_t* part = tb + E + 1;             // [4][kGThreads] partial sums of the group-count scan
     int16_t* le = reinterpret_cast<int16_t*>(part + 4 * kGThreads);  // [kRouteTokensPerGroup * k]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = blockIdx.x;
@@ -583,7 +630,7 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int
             part[kGThreads + tid] = ptot_;
             part[2 * kGThreads + tid] = lt;
             part[3 * kGThreads + tid] = plt;
-            __syncthreads();
+            lds_barrier();
             if (tid < min(E - e0, kGThreads)) {
                 int a = 0, b = 0, c = 0, d = 0;
                 for (int q = 0; q < nsl; ++q) {  // slice q of expert e0 + tid sits at thread q * E + tid
@@ -599,7 +646,7 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int
                 gh[e] = c;
                 gp[e] = d;
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
     // exclusive scans over experts (E <= 512 = 2 * kGThreads): thread t owns experts 2t and 2t+1
@@ -612,9 +659,9 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int
         padded = pad0 + pad1;
         pulls = p0 + p1;
         cnt = c0 + c1;
-        const int incl_pad = block_inclusive_scan(padded, scratch);
-        const int incl_pull = block_inclusive_scan(pulls, scratch);
-        const int incl_cnt = block_inclusive_scan(cnt, scratch);
+        int sv[3] = {padded, pulls, cnt};
+        block_inclusive_scan_n<3>(sv, scratch);
+        const int incl_pad = sv[0], incl_pull = sv[1], incl_cnt = sv[2];
         if (e0 < E) { soff[e0 + 1] = incl_pad - pad1; pbase[e0 + 1] = incl_pull - p1; }
         if (e1 < E) { soff[e1 + 1] = incl_pad; pbase[e1 + 1] = incl_pull; }
         if (tid == 0) { soff[0] = 0; pbase[0] = 0; }
@@ -629,7 +676,7 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (g == 0)
         for (int e = tid; e <= E; e += kGThreads) p.offsets[e] = soff[e];
 
@@ -642,7 +689,7 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int
     const int tt = t0 + lane;
     const int emin = tt < t1 ? smallest_in(le, tt - tg0, k, E) : E;
     if (emin < E) atomicAdd(&wp[w * E + emin], 1);
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < E; e += kGThreads) {
         int run = soff[e] + gh[e], prun = pbase[e] + gp[e];
         for (int ww = 0; ww < kGWaves; ++ww) {
@@ -653,7 +700,7 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int
             prun += cq;
         }
     }
-    __syncthreads();
+    lds_barrier();
     const int64_t hg0 = (int64_t)tg0 * k;
     for (int base = l0; base < l1; base += 64) {
         const int i = base + lane;
@@ -714,7 +761,7 @@ hipError_t launch_route(const moe_shape& s, const int64_t* topk_idx, const PlanP
     hipLaunchKernelGGL(route_count_kernel, dim3(groups), dim3(kGThreads), (size_t)2 * E * 4 + le_bytes, stream,
                        topk_idx, s.num_tokens, s.topk, E, s.expert_begin, groups, p.group_counts);
     if ((int64_t)groups * E <= kFusedScanMaxWords) {
-        const size_t lds = (size_t)(2 * kGWaves * E + 6 * E + 3 + 64 + 4 * kGThreads) * 4 + le_bytes;
+        const size_t lds = (size_t)(2 * kGWaves * E + 6 * E + 3 + 192 + 4 * kGThreads) * 4 + le_bytes;
         hipLaunchKernelGGL(route_scatter_scan_kernel, dim3(groups), dim3(kGThreads), lds, stream, topk_idx,
                            s.num_tokens, s.topk, E, s.expert_begin, groups, s.block_m, p.group_counts, p);
         return hipGetLastError();
