@@ -212,12 +212,12 @@ MOE_API int moe_forward_workspace_bytes(const moe_shape* shape, size_t* bytes);
  *              q = (p & 3) ^ ((c >> 1) & 3);
  *   w_sf_tiled [E][N/256][K/128][256 columns][4 B]: the column's four
  *              scale bytes for that K-step;
- *   tile column c of block nt (c = 64G + 16b + j, b < 4, j < 16) holds
- *   weight row nt*256 + src(c):
- *     which = 1: src = 16*(ch/8) + ch%8 + (j >= 8 ? 8 : 0) with
+ *   tile column c of block nt holds weight row nt*256 + src(c):
+ *     which = 1 (c = 64G + 16b + j, b < 4, j < 16):
+ *                src = 16*(ch/8) + ch%8 + (j >= 8 ? 8 : 0) with
  *                ch = 32G + 4*(j%8) + b (gate row of channel ch for
  *                j < 8, its up row otherwise);
- *     which = 2: src = 64G + 4j + b.
+ *     which = 2 (c = 128S + 16b + j, b < 8, j < 16): src = 128S + 8j + b.
  * Enqueued on `stream`; buffers owned by the caller; in and out must not
  * overlap. */
 MOE_API int moe_prepare_weights(const moe_shape* shape, int which,

@@ -412,7 +412,8 @@ __device__ __forceinline__ void mfma_step(v4f (&acc)[MI][NI], const Frags<MI, NI
 // column (a multiple of 64).  The weight tiling permutes columns so that, in
 // a 64-column group, MFMA block b = ni % 4 gives lane l the output
 // 4*(l & 7) + b of the group's 32 SwiGLU channels (Linear1, gate in lanes
-// l & 8 == 0, up in the others) or 4*(l & 15) + b of its 64 columns (Linear2).
+// l & 8 == 0, up in the others), and in a 128-column span block b = 0..7
+// gives lane l output 8*(l & 15) + b of the span (Linear2).
 // PARTIAL: tiles may end before row BM (M-tiles span several routing blocks);
 // otherwise every tile has BM valid rows and the row checks compile away.
 // COHERENT: the stores are device-scope (sc1) stores, complete at device scope
@@ -497,22 +498,27 @@ __device__ __forceinline__ void epilogue_linear1(const v4f (&acc)[MI][NI], const
 template <int BM, int MI, int NI, bool PARTIAL>
 __device__ __forceinline__ void epilogue_linear2(const v4f (&acc)[MI][NI], const GemmArgs& g, int m0, int rows,
                                                  int wrow0, int gcol0, const int* row_tok, int lane) {
-    static_assert(NI % 4 == 0, "a wave owns whole 64-column groups");
+    static_assert(NI == 4 || NI == 8, "a wave owns half or all of a 128-column span");
+    // W2's tiling puts output column 128S + 8j + b in block b of span S, lane j: a lane's NI blocks are
+    // NI adjacent outputs starting at this column (16 bytes for a whole span, 8 for half of one)
+    const uint32_t col0 = (uint32_t)((gcol0 & ~127) + 8 * (lane & 15) + ((gcol0 & 127) >> 4));
+    // the tile's first row is added to the base in 64 bits (uniform: cap * H * 2 may pass 2^32),
+    // the lane's offset inside the tile in 32 bits
+    uint8_t* out = reinterpret_cast<uint8_t*>(g.out_bf16) + (size_t)(uint32_t)m0 * (uint32_t)g.N * 2u;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int row_local = wrow0 + mi * 16 + 4 * (lane >> 4) + i;
             if ((PARTIAL && row_local >= rows) || row_tok[row_local] < 0) continue;  // padding rows are never read
-            // the tile's first row is added to the base in 64 bits (uniform: cap * H * 2 may pass 2^32),
-            // the lane's offset inside the tile in 32 bits
-            const uint32_t off = ((uint32_t)row_local * (uint32_t)g.N + (uint32_t)(gcol0 + 4 * (lane & 15))) * 2u;
-            uint8_t* out = reinterpret_cast<uint8_t*>(g.out_bf16) + (size_t)(uint32_t)m0 * (uint32_t)g.N * 2u;
-#pragma unroll
-            for (int grp = 0; grp < NI / 4; ++grp) {
-                const uint32_t lo = pack_bf16(acc[mi][grp * 4 + 0][i], acc[mi][grp * 4 + 1][i]);
-                const uint32_t hi = pack_bf16(acc[mi][grp * 4 + 2][i], acc[mi][grp * 4 + 3][i]);
-                *reinterpret_cast<uint2*>(out + (off + (uint32_t)(grp * 128))) = uint2{lo, hi};
+            const uint32_t off = ((uint32_t)row_local * (uint32_t)g.N + col0) * 2u;
+            if constexpr (NI == 8) {
+                *reinterpret_cast<uint4*>(out + off) =
+                    uint4{pack_bf16(acc[mi][0][i], acc[mi][1][i]), pack_bf16(acc[mi][2][i], acc[mi][3][i]),
+                          pack_bf16(acc[mi][4][i], acc[mi][5][i]), pack_bf16(acc[mi][6][i], acc[mi][7][i])};
+            } else {
+                *reinterpret_cast<uint2*>(out + off) =
+                    uint2{pack_bf16(acc[mi][0][i], acc[mi][1][i]), pack_bf16(acc[mi][2][i], acc[mi][3][i])};
             }
         }
 }

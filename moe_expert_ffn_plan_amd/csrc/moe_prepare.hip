@@ -15,15 +15,16 @@
 //
 // Tile column c of a 256-column block holds weight row nt*256 + src(c).  The
 // permutation is chosen for the GEMM epilogues: an MFMA output lane owns one
-// column of each 16-column block, so within every 64-column group the
-// columns are ordered so that one lane's four blocks hold four adjacent
-// outputs (c = 64G + 16b + j, b = 0..3, j = 0..15):
-//   Linear1 (N = 2I, rows interleaved gate/up by 8): lanes j < 8 hold the
-//     gate and lanes j + 8 the up row of channel 32G + 4(j & 7) + b, so the
-//     two halves of a 16-lane row pair up and a lane ends with four adjacent
-//     FP8 outputs (one dword);
-//   Linear2 (N = H): column 64G + 4j + b, so a lane owns four adjacent BF16
-//     outputs (8 bytes).
+// column of each 16-column block, so the columns are ordered so that one
+// lane's blocks hold adjacent outputs:
+//   Linear1 (N = 2I, rows interleaved gate/up by 8; c = 64G + 16b + j,
+//     b = 0..3, j = 0..15): lanes j < 8 hold the gate and lanes j + 8 the up
+//     row of channel 32G + 4(j & 7) + b, so the two halves of a 16-lane row
+//     pair up and a lane ends with four adjacent FP8 outputs (one dword);
+//   Linear2 (N = H; c = 128S + 16b + j, b = 0..7, j = 0..15): column
+//     128S + 8j + b, so a lane that owns all eight blocks of a 128-column
+//     span holds eight adjacent BF16 outputs (16 bytes), and one that owns
+//     four of them (a 64-column wave tile) holds four (8 bytes).
 //
 // Linear2's activation scales use the analogous per-row-block layout
 //   [R/BM][K/128][BM rows][4 B],
@@ -43,7 +44,8 @@ __device__ __forceinline__ int tile_source_col(int which, int c) {
         const int ch = G * 32 + (j & 7) * 4 + b;           // SwiGLU channel within the block
         return (ch >> 3) * 16 + (ch & 7) + (j & 8);        // its gate (j < 8) or up row
     }
-    return G * 64 + j * 4 + b;
+    const int S = c >> 7, b8 = (c >> 4) & 7;
+    return S * 128 + j * 8 + b8;
 }
 
 __global__ __launch_bounds__(kThreads) void tile_weight_data_kernel(const uint8_t* __restrict__ w, int which, int N,

@@ -126,11 +126,12 @@ def test_forward_tp_slice_full(gpu):
 def _tile_columns(which):
     """Weight row (within a 256-row block) stored at each tile column, as documented in moe.h."""
     c = np.arange(256)
-    G, b, j = c >> 6, (c >> 4) & 3, c & 15
     if which == 1:
+        G, b, j = c >> 6, (c >> 4) & 3, c & 15
         ch = 32 * G + 4 * (j & 7) + b                  # SwiGLU channel; gate rows for j < 8, up rows for j >= 8
         return (ch // 8) * 16 + (ch % 8) + 8 * (j >= 8)
-    return 64 * G + 4 * j + b
+    S, b, j = c >> 7, (c >> 4) & 7, c & 15
+    return 128 * S + 8 * j + b
 
 
 def _tile_reference(w, w_sf, N, K, which):
