@@ -201,12 +201,13 @@ constexpr int kSingleWorkgroupHits = 4096;
 __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restrict__ ids, int T, int k, int E,
                                                          int expert_begin, int bm, PlanPtrs p) {
     __shared__ int16_t le[kSingleMaxHits];        // local expert of every hit, -1 if not local
-    __shared__ int32_t wcnt[kWaves * kMaxExperts]; // per-wave counters, later per-wave bases
+    __shared__ int32_t wcnt[kWaves * kMaxExperts]; // per-wave hit counters, later per-wave bases
+    __shared__ int32_t wpc[kWaves * kMaxExperts];  // per-wave pull counters, later per-wave bases
     __shared__ int32_t soff[kMaxExperts + 1];      // padded offsets
-    __shared__ int32_t scnt[kMaxExperts];          // counts (later pull counts)
-    __shared__ int32_t sbase[kMaxExperts + 1];     // pull-order bases
+    __shared__ int32_t scnt[kMaxExperts];          // counts
+    __shared__ int32_t sbase[kMaxExperts + 1];     // pull totals, then pull-order bases
     __shared__ int32_t tb[kMaxExperts + 1];        // M-tile bases per expert
-    __shared__ int32_t scratch[128];
+    __shared__ int32_t scratch[192];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     const int64_t begin = expert_begin;
@@ -226,10 +227,14 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
             if (h < nh) le[h] = (int16_t)((v[u] >= 0 && v[u] < E) ? v[u] : -1);
         }
     }
-    for (int i = tid; i < kWaves * E; i += kThreads) wcnt[i] = 0;
+    for (int i = tid; i < kWaves * E; i += kThreads) {
+        wcnt[i] = 0;
+        wpc[i] = 0;
+    }
     lds_barrier();
 
-    // ---- pass 1: hits per (wave, expert); wave w owns the contiguous hits [h0, h1)
+    // ---- pass 1: hits per (wave, expert), wave w owning the contiguous hits [h0, h1); and tokens per
+    // (wave, smallest local expert), wave w owning the contiguous tokens [t0, t1) (for the pull order)
     const int per_wave = (nh + kWaves * 64 - 1) / (kWaves * 64) * 64;
     const int h0 = min(nh, w * per_wave);
     const int h1 = min(nh, h0 + per_wave);
@@ -237,26 +242,45 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
         const int e = le[h];
         if (e >= 0) atomicAdd(&wcnt[w * E + e], 1);
     }
+    const int tper = (T + kWaves * 64 - 1) / (kWaves * 64) * 64;
+    const int t0 = min(T, w * tper), t1 = min(T, t0 + tper);
+    auto smallest = [&](int t) {
+        int emin = E;
+        for (int j = 0; j < k; ++j) {
+            const int e = le[t * k + j];
+            if (e >= 0 && e < emin) emin = e;
+        }
+        return emin;
+    };
+    for (int base = t0; base < t1; base += 64) {
+        const int t = base + lane;
+        const int emin = t < t1 ? smallest(t) : E;
+        if (emin < E) atomicAdd(&wpc[w * E + emin], 1);
+    }
     lds_barrier();
 
-    // ---- pass 2: per-wave bases, counts, padded offsets
+    // ---- pass 2: per-wave bases, counts, padded offsets, pull bases
     wave_prefix<kWaves>(wcnt, E, scnt);
+    wave_prefix<kWaves>(wpc, E, sbase + 1);  // pull totals for now
     lds_barrier();
     const int cnt = tid < E ? scnt[tid] : 0;
-    int sv[2] = {(cnt + bm - 1) / bm * bm, cnt};
-    block_inclusive_scan_n<2>(sv, scratch);
-    const int incl_pad = sv[0], incl_cnt = sv[1];
+    int sv[3] = {(cnt + bm - 1) / bm * bm, cnt, tid < E ? sbase[tid + 1] : 0};
+    block_inclusive_scan_n<3>(sv, scratch);
+    const int incl_pad = sv[0], incl_cnt = sv[1], incl_pull = sv[2];
     if (tid < E) {
         soff[tid + 1] = incl_pad;
+        sbase[tid + 1] = incl_pull;
         p.counts[tid] = cnt;
         p.offsets[tid + 1] = incl_pad;
     }
     if (tid == 0) {
         soff[0] = 0;
+        sbase[0] = 0;
         p.offsets[0] = 0;
     }
     if (tid == E - 1) {
         p.scalars[0] = incl_pad;        // R_pad
+        p.scalars[1] = incl_pull;       // n_pull
         p.scalars[2] = incl_cnt;        // N
         p.scalars[3] = incl_pad / bm;   // n_blocks
     }
@@ -304,33 +328,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
     write_tile_lists(soff, E, bm, tb, p, 0, 1, true);
     lds_barrier();
 
-    // ---- pass 5: pull order = tokens with a hit, by smallest local expert, then t
-    for (int i = tid; i < kWaves * E; i += kThreads) wcnt[i] = 0;
-    lds_barrier();
-    const int tper = (T + kWaves * 64 - 1) / (kWaves * 64) * 64;
-    const int t0 = min(T, w * tper), t1 = min(T, t0 + tper);
-    auto smallest = [&](int t) {
-        int emin = E;
-        for (int j = 0; j < k; ++j) {
-            const int e = le[t * k + j];
-            if (e >= 0 && e < emin) emin = e;
-        }
-        return emin;
-    };
-    for (int base = t0; base < t1; base += 64) {
-        const int t = base + lane;
-        const int emin = t < t1 ? smallest(t) : E;
-        if (emin < E) atomicAdd(&wcnt[w * E + emin], 1);
-    }
-    lds_barrier();
-    wave_prefix<kWaves>(wcnt, E, scnt);  // counts are no longer needed; scnt takes the pull counts
-    lds_barrier();
-    const int pc = tid < E ? scnt[tid] : 0;
-    const int incl_pull = block_inclusive_scan(pc, scratch);
-    if (tid < E) sbase[tid + 1] = incl_pull;
-    if (tid == 0) sbase[0] = 0;
-    if (tid == E - 1) p.scalars[1] = incl_pull;  // n_pull
-    lds_barrier();
+    // ---- pass 5: pull order = tokens with a hit, by smallest local expert, then t (bases from pass 2)
     for (int base = t0; base < t1; base += 64) {
         const int t = base + lane;
         const int emin = t < t1 ? smallest(t) : E;
@@ -338,9 +336,9 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
         const uint64_t peers = match_peers(valid, emin, nbits);
         if (valid) {
             const int rank = __popcll(peers & lanes_lt());
-            const int cur = wcnt[w * E + emin];
+            const int cur = wpc[w * E + emin];
             p.pull_order[sbase[emin] + cur + rank] = t;
-            if (rank == 0) wcnt[w * E + emin] = cur + __popcll(peers);
+            if (rank == 0) wpc[w * E + emin] = cur + __popcll(peers);
         }
     }
 }
