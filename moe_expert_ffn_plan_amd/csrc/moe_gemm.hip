@@ -152,8 +152,8 @@ __device__ __forceinline__ int fresh_lane() {
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
     asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
-// The same with the non-temporal hint: for operands streamed once (the weights of 16-row tiles, where
-// each weight tile serves one M-tile), so they do not displace reused data in the caches.
+// The same with the non-temporal hint: for operands streamed about once (weight tiles of batches with
+// few rows per expert), so they do not displace reused data in the caches.
 __device__ __forceinline__ void dma16_stream(uint32_t voff, const void* sbase, uint32_t lds) {
     asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
@@ -256,12 +256,13 @@ struct StageLayout {
     static constexpr int SB_INSTR = SB_WORDS / 64;
 };
 
-// DMA sources of one wave.  The A side (rows and their scales) is split over
+// DMA sources of one wave (STREAM: weight tiles loaded with the non-temporal hint, see issue_b_blocks).
+// The A side (rows and their scales) is split over
 // `anw` waves, the B side (weights and their scales) over `bnw` waves; where
 // an operand has fewer instructions than waves, waves repeat one, writing
 // the same bytes to the same place.  Bases are wave-uniform (SGPRs); only the
 // per-lane offsets live in VGPRs.
-template <int BM, int BN, int A_PW, int B_PW, int SB_PW>
+template <int BM, int BN, int A_PW, int B_PW, int SB_PW, bool STREAM>
 struct StageDma {
     using L = StageLayout<BM, BN>;
     uint32_t a_off[A_PW];  // gathered row * K + chunk
@@ -325,17 +326,19 @@ struct StageDma {
         }
         dma4(sa_off, a_sf + (size_t)kt * sa_kt, lds_addr(st + L::A_BYTES + L::B_BYTES + sa_blk * 256));
     }
-    // weight blocks OFF + i * bnw + bw, i < NB (1 KiB each, 16 per 256 columns); 16-row tiles
-    // stream them non-temporally (measured on the decode shape: the weight-bound GEMMs ran 13% faster).
-    // For 128-row tiles, whose weight tiles serve the other M-tiles of their expert, the hint cost 2-6%
-    // where experts span many M-tiles, and choosing it per tile cost 2-3% in the issue path itself.
+    // weight blocks OFF + i * bnw + bw, i < NB (1 KiB each, 16 per 256 columns).  Instances for routing
+    // blocks below the M-tile (block_m < 128: batches with few rows per expert, whose weight tiles serve
+    // one or two M-tiles) stream them non-temporally: measured, the decode shape's GEMMs ran 13% faster,
+    // prefill's 4% (its combine too, the slot rows staying cached), a 1024-token decode batch 8%.  With
+    // block_m = 128 the hint cost 2-6% where experts span many M-tiles, and choosing it per tile at run
+    // time cost 2-3% in the issue path itself.
     template <int NB, int OFF>
     __device__ __forceinline__ void issue_b_blocks(uint8_t* st, int kt, int lane) const {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
             const int blk = OFF + i * bnw + bw;
             const uint8_t* src = b + ((size_t)((blk >> 4) * KT + kt) * 16 + (blk & 15)) * 1024;
-            if constexpr (BM == 16) dma16_stream((uint32_t)lane * 16, src, lds_addr(st + L::A_BYTES + blk * 1024));
+            if constexpr (STREAM) dma16_stream((uint32_t)lane * 16, src, lds_addr(st + L::A_BYTES + blk * 1024));
             else dma16((uint32_t)lane * 16, src, lds_addr(st + L::A_BYTES + blk * 1024));
         }
     }
@@ -576,7 +579,7 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
     const int KT = g.K / kBK;
     load_row_tables<BM, L1>(g, t, row_w, row_tok, tid);
 
-    StageDma<BM, 256, C::A_PW, C::B_PW, C::SB_PW> dma;
+    StageDma<BM, 256, C::A_PW, C::B_PW, C::SB_PW, BM == 16 || PARTIAL> dma;
     dma.init_a(g, t.m, t.rows, row_tok, L1, w, 4);
     dma.init_b(g, t, w, 4);
     auto issue = [&](int kt) {
@@ -773,7 +776,7 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
     wait_and_barrier<0>();
 
     if (grp == 0) {
-        StageDma<BM, 512, 1, C::B0_PW, C::SB_PW> dma;
+        StageDma<BM, 512, 1, C::B0_PW, C::SB_PW, BM == 16 || PARTIAL> dma;
         dma.init_b(g, t0, wq, 4);
         // stage s (and the table load that rides with it) for compute step gs = s - (NS - 1)
         auto issue = [&](int s) {
@@ -814,7 +817,7 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
         }
         if constexpr (FUSED) __syncthreads();  // B_2S
     } else {
-        StageDma<BM, 512, C::A_PW, 1, 1> dma;
+        StageDma<BM, 512, C::A_PW, 1, 1, BM == 16 || PARTIAL> dma;
         // fused Linear2: wait until every Linear1 tile of t's M-tile is done.  The flags came with
         // the row tables; while one is not set yet, sleep and load them again (the wait for that load
         // drains this wave's DMA queue, which only makes the later vmcnt waits conservative)
