@@ -30,9 +30,10 @@
 //  * Weights and their scales come pre-tiled (moe_prepare.hip): a stage's B
 //    is one contiguous block already in LDS order, so every DMA instruction
 //    moves 1 KiB of contiguous memory, and the columns are permuted so that
-//    each lane's outputs of four 16-column blocks are adjacent in memory:
-//    the epilogues store dwords (FP8) or 8-byte runs (BF16) straight from
-//    the accumulators.  A chunks are XOR-swizzled in LDS (chunk ^ ((row >> 1)
+//    each lane's outputs are adjacent in memory: four channels of a 64-column
+//    group in Linear1 (one FP8 dword), eight columns of a 128-column span in
+//    Linear2 (a 16-byte BF16 run; 8 bytes for 64-column wave tiles), stored
+//    straight from the accumulators.  A chunks are XOR-swizzled in LDS (chunk ^ ((row >> 1)
 //    & 7)), B chunks by the tiling (chunk ^ ((col >> 1) & 3)).  Measured on
 //    the device, a ds_read_b128 runs without bank conflicts when the lanes
 //    l, l^2, l^4, l^6 of each group address distinct 16-byte slots modulo
@@ -44,16 +45,16 @@
 //    reads its next fragments from LDS and issues its share of the DMA, and
 //    every phase change is a workgroup barrier.  The two waves sharing a
 //    SIMD are thus never both waiting on LDS, which a single group of
-//    barrier-synchronised waves cannot avoid.  Group 0 streams the weights,
-//    group 1 the activation rows.  256-column tiles (small N) use one group
-//    of four waves that reads, then multiplies.
-//  * Tiles come from a list (expert by expert; for each N-tile all M-tiles
-//    of the expert).  An M-tile spans up to 128 rows, several routing blocks
-//    of one expert, so a weight tile is fetched once per 128 rows rather
-//    than once per block; rows past the expert's end are masked.  blockIdx
-//    is remapped so that each XCD (blockIdx % 8
-//    on MI300-class parts) runs a contiguous run of that list: the M-tiles
-//    sharing a weight tile run together on one XCD and hit its L2.
+//    barrier-synchronised waves cannot avoid.  Group 0 streams most of the
+//    weights, group 1 the activation rows and the rest of the weights.
+//    256-column tiles (small N) use one group of four waves that reads, then
+//    multiplies.
+//  * Tiles come from a list (expert by expert, M-tile by M-tile, all N-tiles
+//    of each).  An M-tile spans up to 128 rows, several routing blocks of one
+//    expert, so a weight tile is fetched once per 128 rows rather than once
+//    per block; rows past the expert's end are masked.  blockIdx is remapped
+//    so that each XCD (blockIdx % 8) runs a contiguous range of M-tiles: the
+//    M-tiles sharing a weight tile run together on one XCD and hit its L2.
 #include "moe_internal.h"
 
 #include <algorithm>

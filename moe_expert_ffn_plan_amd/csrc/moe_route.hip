@@ -8,26 +8,28 @@
 // expert follow ascending flat hit order t*k + j, so the tables are
 // deterministic (the pages' kernels take slots with atomics instead).
 //
-// Design: one 1024-thread workgroup (16 waves) for up to 32768 hits.  The
+// Design: one 1024-thread workgroup (16 waves) for up to 4096 hits.  The
 // local expert id of every hit is first staged in LDS as int16; every later
-// pass reads it from there.  Each wave owns a contiguous range of hits.  Pass
-// 1 counts hits per (wave, expert) with LDS atomics;
-// pass 2 turns those into per-wave bases with a scan over waves and a
-// block-wide scan over experts; pass 3 re-walks each wave's hits in order,
-// 64 at a time, and ranks equal experts inside the batch with a ballot
-// "match" over the bits of the expert id, so every hit's row is its expert's
-// base plus the number of earlier hits of that expert.  The pull order is a
-// second counting sort of tokens keyed by their smallest local expert (a
-// token's smallest slot lies in the range of its smallest expert, and tokens
-// of one expert are in ascending t there).
+// pass reads it from there.  Each wave owns a contiguous range of hits (and
+// of tokens, for the pull order).  Pass 1 counts hits per (wave, expert) and
+// tokens per (wave, smallest local expert) with LDS atomics; pass 2 turns
+// those into per-wave bases with a scan over waves and block-wide scans over
+// experts; pass 3 re-walks each wave's hits in order, 64 at a time, and
+// ranks equal experts inside the batch with a ballot "match" over the bits
+// of the expert id, so every hit's row is its expert's base plus the number
+// of earlier hits of that expert.  The pull order is the same counting sort
+// of tokens keyed by their smallest local expert (a token's smallest slot
+// lies in the range of its smallest expert, and tokens of one expert are in
+// ascending t there).  The scans use DPP lane moves, not LDS shuffles.
 //
-// Large inputs use three kernels instead, so the work spreads over many CUs:
-// route_count_kernel (per group of 256 tokens: hit counts per expert and
-// pull counts per smallest expert), route_scan_kernel (one workgroup: bases
-// of every group, counts, padded offsets, block tables, padding rows) and
-// route_scatter_kernel (per group: the same stable ballot-match scatter,
-// with each wave owning a contiguous 64-token slice).  Both paths produce
-// identical tables.
+// Larger inputs spread over many CUs in groups of kRouteTokensPerGroup
+// tokens: route_count_kernel (per group: hit counts per expert and pull
+// counts per smallest expert), then route_scatter_scan_kernel (per group:
+// the bases of its group from the counts of all groups, the counts, padded
+// offsets, block tables and tile lists, and the same stable ballot-match
+// scatter).  Beyond kFusedScanMaxWords group x expert counters the scan runs
+// as one workgroup of its own (route_scan_kernel) between the counting and
+// the scatter (route_scatter_kernel).  All paths produce identical tables.
 #include "moe_internal.h"
 
 namespace moe {
