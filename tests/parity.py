@@ -73,18 +73,22 @@ def fp8_ulp_distance(q_gpu, sf_gpu, q_ref, sf_ref):
     return np.abs(vg - vr) / (ulp * scale)
 
 
-def assert_fp8_gate(q_gpu, sf_gpu, q_ref, sf_ref, cancel=None, what=""):
-    """The FP8 gate above; `cancel` marks elements with near-total cancellation in Linear1."""
+def assert_fp8_gate(q_gpu, sf_gpu, q_ref, sf_ref, cancel=None, what="", rate=True):
+    """The FP8 gate above; `cancel` marks elements with near-total cancellation in Linear1.  Returns
+    (elements whose code or scale differs, elements compared).  rate=False checks only the 1-ulp clause,
+    for callers that apply the 0.1% to elements pooled over several small cases (on a few thousand
+    elements one mismatch more or less moves the fraction by several hundredths of a percent)."""
     if q_ref.size == 0:
-        return
+        return 0, 0
     code_bad = (e4m3_step_distance(q_gpu, q_ref) > 0) | np.repeat(sf_gpu != sf_ref, 32, axis=1)
     frac = float(code_bad.mean())
     dist = fp8_ulp_distance(q_gpu, sf_gpu, q_ref, sf_ref)
     judged = dist if cancel is None else dist[~cancel]
     worst = float(judged.max()) if judged.size else 0.0
-    assert frac <= 1e-3 and worst <= 1.0, (
+    assert (frac <= 1e-3 or not rate) and worst <= 1.0, (
         f"{what}: FP8 mismatch on {frac:.4%} of elements, worst {worst:.2f} ulp outside cancellation "
         f"(scale mismatches {int((sf_gpu != sf_ref).sum())})")
+    return int(code_bad.sum()), int(code_bad.size)
 
 
 def linear1_cancellation(a_rows, w1_rows_deq):

@@ -38,7 +38,7 @@ def run_gpu(w, d, dev, expert_begin=0, separate_plan=True, swiglu_limit=0.0, exa
             "plan": gpu_plan_to_numpy(pv, T, w.topk)}
 
 
-def check_full(w, d_cpu, out, expert_begin=0, swiglu_limit=0.0):
+def check_full(w, d_cpu, out, expert_begin=0, swiglu_limit=0.0, fp8_rate=True):
     d = inputs.to_numpy(d_cpu)
     ref = forward_ref(d["x"], d["x_sf"], d["topk_idx"] - expert_begin, d["topk_w"], d["w1"], d["w1_sf"], d["w2"],
                       d["w2_sf"], num_experts=w.num_experts, expert_begin=0, block_m=w.block_m,
@@ -53,8 +53,8 @@ def check_full(w, d_cpu, out, expert_begin=0, swiglu_limit=0.0):
             tok = p.row_token[rows]
             cancel[rows] = linear1_cancellation(dequant_fp8_rows(d["x"][tok], d["x_sf"][tok]),
                                                 dequant_fp4_rows(d["w1"][e], d["w1_sf"][e]))
-    assert_fp8_gate(out["h_q"][:p.r_pad][valid], out["h_sf"][:p.r_pad][valid], ref["h_q"][valid],
-                    ref["h_sf"][valid], cancel[valid], w.name)
+    ref["fp8_counts"] = assert_fp8_gate(out["h_q"][:p.r_pad][valid], out["h_sf"][:p.r_pad][valid],
+                                        ref["h_q"][valid], ref["h_sf"][valid], cancel[valid], w.name, rate=fp8_rate)
     assert_y_gate(out["y"], ref["y"], w.name)
     return ref
 
