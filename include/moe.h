@@ -214,9 +214,9 @@ MOE_API int moe_forward_workspace_bytes(const moe_shape* shape, size_t* bytes);
  *              scale bytes for that K-step;
  *   tile column c of block nt holds weight row nt*256 + src(c):
  *     which = 1 (c = 64G + 16b + j, b < 4, j < 16):
- *                src = 16*(ch/8) + ch%8 + (j >= 8 ? 8 : 0) with
- *                ch = 32G + 4*(j%8) + b (gate row of channel ch for
- *                j < 8, its up row otherwise);
+ *                src = 16*(ch/8) + ch%8 + (b >= 2 ? 8 : 0) with
+ *                ch = 32G + 2j + b%2 (gate row of channel ch for
+ *                b < 2, its up row otherwise);
  *     which = 2 (c = 128S + 16b + j, b < 8, j < 16): src = 128S + 8j + b.
  * Enqueued on `stream`; buffers owned by the caller; in and out must not
  * overlap. */

@@ -113,21 +113,42 @@ __device__ __forceinline__ float pow2_neg(int code) {  // 2^(127 - code), code i
     return __uint_as_float((uint32_t)(254 - code) << 23);
 }
 
-// Cross-lane moves inside a 16-lane row (DPP, no LDS round trip).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-constexpr int kDppRor8 = 0x128;        // lane i <- lane (i + 8) % 16: swaps the two halves of a row
-constexpr int kDppXor1 = 0xB1;         // quad_perm [1, 0, 3, 2]
-constexpr int kDppXor2 = 0x4E;         // quad_perm [2, 3, 0, 1]
-constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7 - i within each group of 8
+// Cross-lane moves inside a 16-lane row (DPP, no LDS round trip).  Every control used here stays
+// inside the row, so no lane reads out of range.
+constexpr int kDppXor1 = 0xB1;         // lane i <- lane i ^ 1 (quad_perm [1, 0, 3, 2])
+constexpr int kDppXor2 = 0x4E;         // lane i <- lane i ^ 2 (quad_perm [2, 3, 0, 1])
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane i ^ 7 (mirror within each group of 8)
+constexpr int kDppRowMirror = 0x140;   // lane i <- lane i ^ 15 (mirror within the row)
 
-// max over the 8 lanes of each aligned group of 8
-__device__ __forceinline__ float max8(float v) {
-    v = fmaxf(v, dpp<kDppXor1>(v));
-    v = fmaxf(v, dpp<kDppXor2>(v));
-    return fmaxf(v, dpp<kDppHalfMirror>(v));
+// Maxima of non-negative floats are taken on their bit patterns, which order the same way; the
+// integer maximum also needs no NaN quieting of the moved operand, so it fuses with the DPP move.
+template <int CTRL>
+__device__ __forceinline__ uint32_t umax_dpp(uint32_t a, uint32_t b) {
+    return max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)b, CTRL, 0xF, 0xF, true));
+}
+// One step of a transposed maximum: the lane and its partner (which differs from it in the step's
+// split bit) each keep one half of their first N values and take the partner's copy of that half.
+template <int CTRL, int N, int V>
+__device__ __forceinline__ void fold_half(uint32_t (&m)[V], bool upper) {
+#pragma unroll
+    for (int t = 0; t < N / 2; ++t) {
+        const uint32_t keep = upper ? m[t + N / 2] : m[t];
+        const uint32_t send = upper ? m[t] : m[t + N / 2];
+        m[t] = umax_dpp<CTRL>(keep, send);
+    }
+}
+// Maxima over the 16 lanes of each DPP row of V = 4 or 8 non-negative values per lane (as bit
+// patterns): lane j returns the maximum of value j >> (V == 8 ? 1 : 2).  The partners of the four
+// steps (j ^ 15, j ^ 7, j ^ 2, j ^ 1) span all 16 lanes; the first log2(V) steps split on bits 3, 2
+// (and 1) of j, so each halving keeps the values whose index matches those bits.
+template <int V>
+__device__ __forceinline__ float row_max16(uint32_t (&m)[V], int j) {
+    static_assert(V == 4 || V == 8, "four or eight values per lane");
+    fold_half<kDppRowMirror, V>(m, j & 8);
+    fold_half<kDppHalfMirror, V / 2>(m, j & 4);
+    if constexpr (V == 8) fold_half<kDppXor2, 2>(m, j & 2);
+    else m[0] = umax_dpp<kDppXor2>(m[0], m[0]);
+    return __uint_as_float(umax_dpp<kDppXor1>(m[0], m[0]));
 }
 
 // ---- LDS DMA: lane l reads `size` bytes at the wave-uniform base plus its
@@ -414,10 +435,11 @@ __device__ __forceinline__ void mfma_step(v4f (&acc)[MI][NI], const Frags<MI, NI
 // ---- epilogues: straight from the accumulators to global memory.
 // wrow0: the wave's first row within the tile; gcol0: its first global output
 // column (a multiple of 64).  The weight tiling permutes columns so that, in
-// a 64-column group, MFMA block b = ni % 4 gives lane l the output
-// 4*(l & 7) + b of the group's 32 SwiGLU channels (Linear1, gate in lanes
-// l & 8 == 0, up in the others), and in a 128-column span block b = 0..7
-// gives lane l output 8*(l & 15) + b of the span (Linear2).
+// a 64-column group, MFMA blocks k and k + 2 (k = 0, 1; ni % 4) give lane l
+// the gate and the up row of channel 2*(l & 15) + k of the group's 32 SwiGLU
+// channels (Linear1: a lane holds both inputs of its two adjacent outputs),
+// and in a 128-column span block b = 0..7 gives lane l output 8*(l & 15) + b
+// of the span (Linear2).
 // PARTIAL: tiles may end before row BM (M-tiles span several routing blocks);
 // otherwise every tile has BM valid rows and the row checks compile away.
 // COHERENT: the stores are device-scope (sc1) stores, complete at device scope
@@ -430,35 +452,31 @@ template <int BM, int MI, int NI, bool PARTIAL, bool COHERENT, int EPI>
 __device__ __forceinline__ void epilogue_linear1(const v4f (&acc)[MI][NI], const GemmArgs& g, int m0, int rows,
                                                  int wrow0, int gcol0, const float* row_w, const int* row_tok,
                                                  int lane) {
-    static_assert(NI % 4 == 0, "a wave owns whole 64-column groups");
-    const bool gate_lane = (lane & 8) == 0;
-    const int j8 = lane & 7;
+    static_assert(NI == 4 || NI == 8, "a wave owns one or two 64-column groups");
+    constexpr int NG = NI / 4;              // 64-column groups: 32 channels, one UE8M0 scale per row
+    constexpr int V = 4 * NG;               // (group, row) maxima per lane and 16-row block
+    constexpr int VSHIFT = V == 8 ? 1 : 2;  // lane j computes the scale of (group, row) j >> VSHIFT
+    lane = fresh_lane();                    // per-lane values derived here are not kept across the K-loop
+    const int j = lane & 15;
+    const int own = j >> VSHIFT;
+    const int own_grp = own >> 2, own_i = own & 3;
+    const int row_base = (lane & 0x30) * 4;  // ds_bpermute byte address of lane 0 of this DPP row
     const int n_q = g.N / 2;
     const int ksteps2 = g.N / kTileN;  // Linear2 K-steps (128 channels each)
     constexpr float kLog2e = 1.4426950408889634f;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
+        const int row0 = wrow0 + mi * 16 + 4 * (lane >> 4);  // the lane's rows are row0 .. row0 + 3
+        float p[NG][4][2];  // silu(gate) * up of channels 2j and 2j + 1 per group and row
+        uint32_t m[V];      // max |p| of each (group, row), as bit patterns
 #pragma unroll
-        for (int grp = 0; grp < NI / 4; ++grp) {
-            const int gcol = gcol0 + grp * 64;  // first Z column of this 32-channel group
-            // lanes j and j + 8 hold the gate and the up row of one channel: swap halves
-            float other[4][4];
+        for (int grp = 0; grp < NG; ++grp)
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) other[b][i] = dpp<kDppRor8>(acc[mi][grp * 4 + b][i]);
-#pragma unroll
-            for (int ii = 0; ii < 2; ++ii) {
-                // gate lanes finish rows 0-1 of the lane's four, up lanes rows 2-3
-                const int row_local = wrow0 + mi * 16 + 4 * (lane >> 4) + (gate_lane ? ii : 2 + ii);
-                const float wgt = row_tok[row_local] >= 0 ? row_w[row_local] : 0.0f;  // padding rows: h = 0
-                float h[4];
-                float amax = 0.0f;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    // gate and up rounded to BF16 together, then widened back to FP32
-                    const uint32_t gu = pack_bf16(gate_lane ? acc[mi][grp * 4 + b][ii] : other[b][2 + ii],
-                                                  gate_lane ? other[b][ii] : acc[mi][grp * 4 + b][2 + ii]);
+                for (int k = 0; k < 2; ++k) {
+                    // gate (block k) and up (block k + 2) rounded to BF16 together, widened back to FP32
+                    const uint32_t gu = pack_bf16(acc[mi][grp * 4 + k][i], acc[mi][grp * 4 + 2 + k][i]);
                     float gv = __uint_as_float(gu << 16);
                     float uv = __uint_as_float(gu & 0xFFFF0000u);
                     if (EPI == kEpiClamp || (EPI == kEpiExact && g.swiglu_limit > 0.0f)) {  // activation clamp
@@ -470,32 +488,45 @@ __device__ __forceinline__ void epilogue_linear1(const v4f (&acc)[MI][NI], const
                     const float s = EPI == kEpiExact
                                         ? gv / (1.0f + expf(-gv))
                                         : gv * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-gv * kLog2e));
-                    h[b] = (s * uv) * wgt;
-                    amax = fmaxf(amax, fabsf(h[b]));
+                    p[grp][i][k] = s * uv;
                 }
-                amax = max8(amax);
-                const int code = requant_code(amax);
-                const float inv = pow2_neg(code);
-                int q = __builtin_amdgcn_cvt_pk_fp8_f32(h[0] * inv, h[1] * inv, 0, false);
-                q = __builtin_amdgcn_cvt_pk_fp8_f32(h[2] * inv, h[3] * inv, q, true);
-                // 32-bit offsets from uniform bases (cap * I < 2^31 is checked on the host)
+                m[grp * 4 + i] = __float_as_uint(fmaxf(fabsf(p[grp][i][0]), fabsf(p[grp][i][1])));
+            }
+        // The output is h = p * w (w: the row's top-k weight, 0 on padding rows).  Rounding is
+        // monotonic, so max |fl(p w)| = fl(|w| max |p|): the scale comes from the unweighted maximum,
+        // and since the requant factor 2^-s is a power of two, fl(fl(p w) 2^-s) = fl(p fl(w 2^-s)).
+        const float amax_p = row_max16<V>(m, j);
+        const int own_row = row0 + own_i;
+        const float wgt = row_tok[own_row] >= 0 ? row_w[own_row] : 0.0f;
+        const int code = requant_code(amax_p * fabsf(wgt));
+        const float factor = wgt * pow2_neg(code);
+        // 32-bit offsets from uniform bases (cap * I < 2^31 is checked on the host)
+        if ((j & ((1 << VSHIFT) - 1)) == 0 && (!PARTIAL || own_row < rows)) {
+            const int gcol = gcol0 + own_grp * 64;  // first Z column of the 32-channel group
+            // Linear2 K-step = 256-column block of Z, byte = 64-column group within it
+            uint8_t* sp = g.out_sf + tile_scale_offset<BM, PARTIAL>(m0, own_row, ksteps2, gcol / kTileN, g.bm_shift) +
+                          (uint32_t)((gcol % kTileN) / 64);
+            if constexpr (COHERENT) __hip_atomic_store(sp, (uint8_t)code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else *sp = (uint8_t)code;
+        }
+#pragma unroll
+        for (int grp = 0; grp < NG; ++grp)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // the factor of (grp, row i) from the first lane that computed it
+                const float f = __int_as_float(
+                    __builtin_amdgcn_ds_bpermute(row_base + ((grp * 4 + i) << VSHIFT) * 4, __float_as_int(factor)));
+                const int q = __builtin_amdgcn_cvt_pk_fp8_f32(p[grp][i][0] * f, p[grp][i][1] * f, 0, false);
+                const int row_local = row0 + i;
                 if (!PARTIAL || row_local < rows) {
                     const uint32_t row = (uint32_t)(m0 + row_local);
-                    int* qp = reinterpret_cast<int*>(g.out_q + (row * (uint32_t)n_q + (uint32_t)(gcol / 2 + 4 * j8)));
-                    // Linear2 K-step = 256-column block of Z, byte = 64-column group within it
-                    uint8_t* sp = g.out_sf + tile_scale_offset<BM, PARTIAL>(m0, row_local, ksteps2, gcol / kTileN,
-                                                                            g.bm_shift) +
-                                  (uint32_t)((gcol % kTileN) / 64);
-                    if constexpr (COHERENT) {
-                        __hip_atomic_store(qp, q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        if (j8 == 0) __hip_atomic_store(sp, (uint8_t)code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    } else {
-                        *qp = q;
-                        if (j8 == 0) *sp = (uint8_t)code;
-                    }
+                    uint16_t* qp = reinterpret_cast<uint16_t*>(
+                        g.out_q + (row * (uint32_t)n_q + (uint32_t)((gcol0 + grp * 64) / 2 + 2 * j)));
+                    if constexpr (COHERENT)
+                        __hip_atomic_store(qp, (uint16_t)q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    else *qp = (uint16_t)q;
                 }
             }
-        }
     }
 }
 

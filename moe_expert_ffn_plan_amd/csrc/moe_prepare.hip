@@ -18,9 +18,10 @@
 // column of each 16-column block, so the columns are ordered so that one
 // lane's blocks hold adjacent outputs:
 //   Linear1 (N = 2I, rows interleaved gate/up by 8; c = 64G + 16b + j,
-//     b = 0..3, j = 0..15): lanes j < 8 hold the gate and lanes j + 8 the up
-//     row of channel 32G + 4(j & 7) + b, so the two halves of a 16-lane row
-//     pair up and a lane ends with four adjacent FP8 outputs (one dword);
+//     b = 0..3, j = 0..15): block b < 2 holds the gate row and block b + 2
+//     the up row of channel 32G + 2j + (b & 1), so a lane holds both inputs
+//     of two adjacent outputs (no cross-lane exchange before the SwiGLU) and
+//     a 64-column group is one 32-channel requant group;
 //   Linear2 (N = H; c = 128S + 16b + j, b = 0..7, j = 0..15): column
 //     128S + 8j + b, so a lane that owns all eight blocks of a 128-column
 //     span holds eight adjacent BF16 outputs (16 bytes), and one that owns
@@ -41,8 +42,8 @@ constexpr int kThreads = 256;
 __device__ __forceinline__ int tile_source_col(int which, int c) {
     const int G = c >> 6, b = (c >> 4) & 3, j = c & 15;
     if (which == 1) {
-        const int ch = G * 32 + (j & 7) * 4 + b;           // SwiGLU channel within the block
-        return (ch >> 3) * 16 + (ch & 7) + (j & 8);        // its gate (j < 8) or up row
+        const int ch = G * 32 + j * 2 + (b & 1);           // SwiGLU channel within the block
+        return (ch >> 3) * 16 + (ch & 7) + (b & 2) * 4;    // its gate (b < 2) or up row
     }
     const int S = c >> 7, b8 = (c >> 4) & 7;
     return S * 128 + j * 8 + b8;

@@ -128,8 +128,8 @@ def _tile_columns(which):
     c = np.arange(256)
     if which == 1:
         G, b, j = c >> 6, (c >> 4) & 3, c & 15
-        ch = 32 * G + 4 * (j & 7) + b                  # SwiGLU channel; gate rows for j < 8, up rows for j >= 8
-        return (ch // 8) * 16 + (ch % 8) + 8 * (j >= 8)
+        ch = 32 * G + 2 * j + (b & 1)                  # SwiGLU channel; gate rows for b < 2, up rows for b >= 2
+        return (ch // 8) * 16 + (ch % 8) + 8 * (b >= 2)
     S, b, j = c >> 7, (c >> 4) & 7, c & 15
     return 128 * S + 8 * j + b
 
