@@ -645,18 +645,22 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
 // operand ring runs on across tile boundaries and the next tile's first
 // stages load while the current one finishes.
 //
-// Phases are separated by workgroup barriers B_0, B_1, ...  Group 0 reads
-// stage gs in phase 2gs and multiplies it in phase 2gs+1; group 1 reads it
-// in phase 2gs+1 and multiplies it in phase 2gs+2.  Stage gs is therefore
-// read between B_2gs and B_2gs+2, so:
-//   * before B_2gs each wave waits for its own share of stage gs (vmcnt);
-//   * stage gs + NS - 1 reuses the buffer of stage gs - 1, which is free
-//     after B_2gs; group 0 issues its share in phase 2gs, group 1 in 2gs+1;
-//   * a wave finishing a read phase waits for its LDS reads (lgkmcnt(0))
-//     before the barrier, so the buffer it read may be refilled after it.
-// Both groups pass the same 2*S barriers (group 1 skips B_2S, which would
-// only separate its last reads from its last MFMAs).  A group runs the
-// epilogue of a tile right after its last MFMA phase of that tile.
+// One workgroup barrier B_gs per K-step.  Between B_gs and B_gs+1 group 0
+// issues its share of stage gs + NS - 1, reads stage gs and multiplies it,
+// while group 1 first multiplies stage gs - 1 (read before B_gs), then
+// issues its share of stage gs + NS - 1 and reads stage gs.  So each group's
+// DMA issue and LDS reads run while the other group's MFMAs occupy the
+// SIMD's matrix core, with no barrier between the two halves: the halves
+// find their own balance, and a barrier costs a few hundred cycles.
+//   * before B_gs each wave waits for its own share of stage gs (vmcnt), so
+//     stage gs is whole after B_gs;
+//   * stage gs + NS - 1 reuses the buffer of stage gs - 1, whose reads all
+//     fall before B_gs: each wave waits for its LDS reads (lgkmcnt(0))
+//     before every barrier.
+// Both groups pass the same S barriers; group 1 multiplies stage S - 1
+// after the last one.  A group runs the epilogue of a tile right after its
+// last MFMAs of that tile (group 1 half a step after group 0, overlapping
+// group 0's next issue, reads and MFMAs).
 //
 // Per-tile tables reach LDS through the same DMA stream, a fixed number of
 // extra instructions per wave per stage so the vmcnt arithmetic stays exact:
@@ -824,20 +828,12 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
         for (int s = 0; s < L::NS - 1; ++s)
             if (s < S) issue(s);
         for (int gs = 0, kt = 0, ci = 0; gs < S; ++gs) {
-            wait_stages_and_barrier<C::D0>(min(L::NS - 2, S - 1 - gs));  // B_2gs
+            wait_stages_and_barrier<C::D0>(min(L::NS - 2, S - 1 - gs));  // B_gs
             if (kt == 0) read_entry(ci, ct);
             if (gs + L::NS - 1 < S) issue(gs + L::NS - 1);
-            // this group's read phase carries its DMA issue as well, so it reads only the first half
-            // of its A fragments here and the second half at the start of its MFMA phase (stage gs is
-            // still intact then: it is refilled only after B_2gs+2)
-            constexpr int MH = C::MI / 2;
-            const uint8_t* st = sh.smem + (gs % L::NS) * L::STAGE;
             Frags<C::MI, C::NI> f;
-            read_frags<BM, 512, C::MI, C::NI, 0, MH>(f, st, wrow0, wcol0, lane);
-            wait_and_barrier<kNoVmWait>();                                 // B_2gs+1
-            read_frags<BM, 512, C::MI, C::NI, MH, C::MI, false>(f, st, wrow0, wcol0, lane);
-            mfma_step<C::MI, C::NI, 0, MH>(acc, f, kt == 0);
-            mfma_step<C::MI, C::NI, MH, C::MI>(acc, f, kt == 0);
+            read_frags<BM, 512>(f, sh.smem + (gs % L::NS) * L::STAGE, wrow0, wcol0, lane);
+            mfma_step(acc, f, kt == 0);
             if (++kt == KT) {
                 epilogue<BM, C::MI, C::NI, L1, PARTIAL, FUSED, EPI>(acc, g, ct, wrow0, ct.n * 512 + wcol0,
                                                                sh.wts[ci % kTableSlots], sh.meta[ci % kTableSlots],
@@ -847,7 +843,7 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
                 ++ci;
             }
         }
-        if constexpr (FUSED) __syncthreads();  // B_2S
+        if constexpr (FUSED) __syncthreads();  // B_S
     } else {
         StageDma<BM, 512, C::A_PW, 1, 1, BM == 16 || PARTIAL> dma;
         // fused Linear2: wait until every Linear1 tile of t's M-tile is done.  The flags came with
@@ -913,21 +909,10 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
 #pragma unroll
         for (int s = 0; s < L::NS - 1; ++s)
             if (s < S) issue(s);
-        wait_stages_and_barrier<C::D1>(min(L::NS - 2, S - 1), starts_tile(0, min(L::NS - 2, S - 1)));  // B_0
-        for (int gs = 0, kt = 0, ci = 0; gs < S; ++gs) {
-            wait_and_barrier<kNoVmWait>();                                 // B_2gs+1
-            if constexpr (FUSED && L1) store_flag();
-            if (kt == 0) {
-                read_entry(ci, ct);
-                read_entry(ci + 1, tn);
-            }
-            if (gs + L::NS - 1 < S) issue(gs + L::NS - 1);
-            Frags<C::MI, C::NI> f;
-            read_frags<BM, 512>(f, sh.smem + (gs % L::NS) * L::STAGE, wrow0, wcol0, lane);
-            if (gs + 1 < S) {  // B_2gs+2
-                const int n = min(L::NS - 2, S - 2 - gs);
-                wait_stages_and_barrier<C::D1>(n, starts_tile(gs + 1, n));
-            }
+        // step gs - 1's product and epilogue, then the issue and the fragment reads of step gs
+        Frags<C::MI, C::NI> f;
+        int kt = 0, ci = 0;
+        auto multiply = [&]() {
             mfma_step(acc, f, kt == 0);
             if (++kt == KT) {
                 epilogue<BM, C::MI, C::NI, L1, PARTIAL, FUSED, EPI>(acc, g, ct, wrow0, ct.n * 512 + wcol0,
@@ -941,9 +926,24 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
                 kt = 0;
                 ++ci;
             }
+        };
+        for (int gs = 0; gs < S; ++gs) {
+            {  // B_gs
+                const int n = min(L::NS - 2, S - 1 - gs);
+                wait_stages_and_barrier<C::D1>(n, starts_tile(gs, n));
+            }
+            if constexpr (FUSED && L1) store_flag();
+            if (gs > 0) multiply();
+            if (kt == 0) {
+                read_entry(ci, ct);
+                read_entry(ci + 1, tn);
+            }
+            if (gs + L::NS - 1 < S) issue(gs + L::NS - 1);
+            read_frags<BM, 512>(f, sh.smem + (gs % L::NS) * L::STAGE, wrow0, wcol0, lane);
         }
+        multiply();  // stage S - 1 (S > 0: a run has at least one tile)
         if constexpr (FUSED) {
-            __syncthreads();  // B_2S
+            __syncthreads();  // B_S
             if constexpr (L1) store_flag();
         }
     }
