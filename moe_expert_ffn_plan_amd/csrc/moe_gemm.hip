@@ -274,17 +274,18 @@ struct StageLayout {
     static_assert(kLdsBudget / STAGE >= 3, "three stages must fit");
     static constexpr int A_INSTR = A_BYTES / 1024;  // 1 KiB per DMA instruction
     static constexpr int B_INSTR = B_BYTES / 1024;
-    static constexpr int SA_INSTR = SA_WORDS / 64;
-    static constexpr int SB_INSTR = SB_WORDS / 64;
+    static constexpr int SA_INSTR = SA_WORDS / 64;   // gathered 4-byte words: 64 rows per instruction
+    static constexpr int SB_INSTR = SB_WORDS / 256;  // contiguous: 256 columns (1 KiB) per instruction
+    static_assert(SA_INSTR + SB_INSTR <= 4, "one scale instruction per A-side wave");
 };
 
 // DMA sources of one wave (STREAM: weight tiles loaded with the non-temporal hint, see issue_b_blocks).
-// The A side (rows and their scales) is split over
-// `anw` waves, the B side (weights and their scales) over `bnw` waves; where
-// an operand has fewer instructions than waves, waves repeat one, writing
-// the same bytes to the same place.  Bases are wave-uniform (SGPRs); only the
-// per-lane offsets live in VGPRs.
-template <int BM, int BN, int A_PW, int B_PW, int SB_PW, bool STREAM>
+// The A side (rows, and all scales) is split over `anw` waves, the weight blocks over `bnw` waves; where
+// an operand has fewer instructions than waves, waves repeat one, writing the same bytes to the same
+// place.  Each A-side wave issues one scale instruction per stage: waves 0 .. SA_INSTR-1 an activation-
+// scale block, the next SB_INSTR waves a weight-scale block, any further wave a repeat of an
+// activation-scale block.  Bases are wave-uniform (SGPRs); only the per-lane offsets live in VGPRs.
+template <int BM, int BN, int A_PW, int B_PW, bool STREAM>
 struct StageDma {
     using L = StageLayout<BM, BN>;
     uint32_t a_off[A_PW];  // gathered row * K + chunk
@@ -293,7 +294,8 @@ struct StageDma {
     const uint8_t* a_sf;
     const uint8_t* b;
     const uint8_t* b_sf;
-    int KT, aw, anw, bw, bnw, sa_blk, sa_kt;
+    int KT, aw, anw, bw, bnw, sa_blk, sa_kt, sb_blk;
+    bool sb_wave;  // this wave's scale instruction loads weight scales
 
     // Linear1 gathers rows and their scales through row_token; its padding
     // rows read token 0 (their top-k weight is 0, so they produce h = 0).
@@ -320,6 +322,8 @@ struct StageDma {
             a_off[i] = (uint32_t)src_row * (uint32_t)g.K + (uint32_t)(c * 16);
         }
         a = static_cast<const uint8_t*>(uniform_ptr(g.a));
+        sb_wave = aw >= L::SA_INSTR && aw < L::SA_INSTR + L::SB_INSTR;
+        sb_blk = aw - L::SA_INSTR;
         sa_blk = aw % L::SA_INSTR;
         const int sa_row = min(sa_blk * 64 + lane, BM - 1);
         a_sf = static_cast<const uint8_t*>(uniform_ptr(g.a_sf));
@@ -346,7 +350,11 @@ struct StageDma {
             const int blk = (i * anw + aw) % L::A_INSTR;
             dma16(a_off[i], a + (size_t)kt * kBK, lds_addr(st + blk * 1024));
         }
-        dma4(sa_off, a_sf + (size_t)kt * sa_kt, lds_addr(st + L::A_BYTES + L::B_BYTES + sa_blk * 256));
+        if (sb_wave)  // weight scales [256 columns][4 B] per 256-column block and K-step, contiguous
+            dma16((uint32_t)lane * 16, b_sf + ((size_t)sb_blk * KT + kt) * 1024,
+                  lds_addr(st + L::A_BYTES + L::B_BYTES + 4 * L::SA_WORDS + sb_blk * 1024));
+        else
+            dma4(sa_off, a_sf + (size_t)kt * sa_kt, lds_addr(st + L::A_BYTES + L::B_BYTES + sa_blk * 256));
     }
     // weight blocks OFF + i * bnw + bw, i < NB (1 KiB each, 16 per 256 columns).  Instances for routing
     // blocks below the M-tile (block_m < 128: batches with few rows per expert, whose weight tiles serve
@@ -364,15 +372,9 @@ struct StageDma {
             else dma16((uint32_t)lane * 16, src, lds_addr(st + L::A_BYTES + blk * 1024));
         }
     }
-    // the first B_PW * bnw weight blocks and all the weight scales
+    // the first B_PW * bnw weight blocks
     __device__ __forceinline__ void issue_b(uint8_t* st, int kt, int lane) const {
         issue_b_blocks<B_PW, 0>(st, kt, lane);
-#pragma unroll
-        for (int i = 0; i < SB_PW; ++i) {
-            const int blk = (i * bnw + bw) % L::SB_INSTR;  // 64 columns per instruction
-            dma4((uint32_t)lane * 4, b_sf + ((size_t)((blk >> 2) * KT + kt) * 256 + (blk & 3) * 64) * 4,
-                 lds_addr(st + L::A_BYTES + L::B_BYTES + 4 * L::SA_WORDS + blk * 256));
-        }
     }
 };
 
@@ -591,8 +593,7 @@ struct Cfg4 {
     static constexpr int MI = WTM / 16, NI = WTN / 16;
     static constexpr int A_PW = L::A_INSTR >= 4 ? L::A_INSTR / 4 : 1;
     static constexpr int B_PW = L::B_INSTR / 4;
-    static constexpr int SB_PW = L::SB_INSTR / 4;
-    static constexpr int D = A_PW + 1 + B_PW + SB_PW;  // DMA instructions per wave per stage
+    static constexpr int D = A_PW + 1 + B_PW;  // DMA instructions per wave per stage
     static_assert(2 * D < 64, "vmcnt range");
 };
 
@@ -611,7 +612,7 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
     const int KT = g.K / kBK;
     load_row_tables<BM, L1>(g, t, row_w, row_tok, tid);
 
-    StageDma<BM, 256, C::A_PW, C::B_PW, C::SB_PW, BM == 16 || PARTIAL> dma;
+    StageDma<BM, 256, C::A_PW, C::B_PW, BM == 16 || PARTIAL> dma;
     dma.init_a(g, t.m, t.rows, row_tok, L1, w, 4);
     dma.init_b(g, t, w, 4);
     auto issue = [&](int kt) {
@@ -701,17 +702,16 @@ struct CfgPP {
     static constexpr int WTN = SPLIT_ROWS ? 128 : 64;
     static constexpr int MI = WTM / 16, NI = WTN / 16;
     // The weight blocks are split between the groups so that their read phases, which carry the
-    // DMA issue, are about as long: group 0 issues B0_PW weight blocks per wave, the weight
-    // scales and the list entry; group 1 the activation rows and their scales, B1_PW weight
-    // blocks per wave and the row tables.  (Measured on tp_slice: without any weight DMA the
+    // DMA issue, are about as long: group 0 issues B0_PW weight blocks per wave and the list
+    // entry; group 1 the activation rows, one scale block per wave (activation or weight
+    // scales), B1_PW weight blocks per wave and the row tables.  (Measured on tp_slice: without any weight DMA the
     // GEMMs ran 13-18% faster, without any row DMA no faster, so the weights-only group was
     // the one the other waited for.)
     static constexpr int A_PW = L::A_INSTR >= 4 ? L::A_INSTR / 4 : 1;
     static constexpr int B_PW = L::B_INSTR / 4;
     static constexpr int B1_PW = A_PW >= 4 ? B_PW / 4 : B_PW / 2;
     static constexpr int B0_PW = B_PW - B1_PW;
-    static constexpr int SB_PW = L::SB_INSTR / 4;
-    static constexpr int D0 = B0_PW + SB_PW + 1;
+    static constexpr int D0 = B0_PW + 1;
     static constexpr bool GATED = FUSED && !L1;  // + the Linear1 flags of the next tile
     static constexpr int D1 = A_PW + B1_PW + 1 + 1 + (GATED ? 1 : 0);  // + 1 on the first stage of each tile (Linear1)
     static constexpr int MIN_KT_PERSISTENT = 2 * (L::NS - 1);
@@ -812,7 +812,7 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
     wait_and_barrier<0>();
 
     if (grp == 0) {
-        StageDma<BM, 512, 1, C::B0_PW, C::SB_PW, BM == 16 || PARTIAL> dma;
+        StageDma<BM, 512, 1, C::B0_PW, BM == 16 || PARTIAL> dma;
         dma.init_b(g, t0, wq, 4);
         // stage s (and the table load that rides with it) for compute step gs = s - (NS - 1)
         auto issue = [&](int s) {
@@ -845,7 +845,7 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
         }
         if constexpr (FUSED) __syncthreads();  // B_S
     } else {
-        StageDma<BM, 512, C::A_PW, 1, 1, BM == 16 || PARTIAL> dma;
+        StageDma<BM, 512, C::A_PW, 1, BM == 16 || PARTIAL> dma;
         // fused Linear2: wait until every Linear1 tile of t's M-tile is done.  The flags came with
         // the row tables; while one is not set yet, sleep and load them again (the wait for that load
         // drains this wave's DMA queue, which only makes the later vmcnt waits conservative)
