@@ -37,7 +37,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
             for (int u = 0; u < kBatch; ++u) {
                 const int r = j0 + u < k ? s[j0 + u] : -1;
                 ok[u] = r >= 0;
-                v[u] = ok[u] ? *reinterpret_cast<const v4i*>(yslot + (size_t)r * H + c * 8) : v4i{0, 0, 0, 0};
+                // slot rows are read exactly once: non-temporal, so they do not evict other lines
+                v[u] = ok[u] ? __builtin_nontemporal_load(reinterpret_cast<const v4i*>(yslot + (size_t)r * H + c * 8))
+                             : v4i{0, 0, 0, 0};
             }
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
@@ -56,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
             const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)acc[2 * q + 1]);
             out[q] = (int)(lo | (hi << 16));
         }
-        *reinterpret_cast<v4i*>(y + (size_t)t * H + c * 8) = out;
+        __builtin_nontemporal_store(out, reinterpret_cast<v4i*>(y + (size_t)t * H + c * 8));
     }
 }
 

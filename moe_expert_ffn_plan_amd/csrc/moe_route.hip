@@ -370,6 +370,27 @@ __device__ __forceinline__ void load_group_experts(const int64_t* __restrict__ i
     }
 }
 
+// The same in two steps, so that other global loads can be in flight together with these: fetch_ids
+// issues the loads of the first 8 * kGThreads hits into registers, store_ids converts and writes them
+// (and handles any further hits as load_group_experts does).
+__device__ __forceinline__ void fetch_ids(const int64_t* __restrict__ ids, int64_t h0, int n, int64_t (&v)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int i = u * kGThreads + threadIdx.x;
+        v[u] = i < n ? ids[h0 + i] : -1;
+    }
+}
+__device__ __forceinline__ void store_ids(const int64_t* __restrict__ ids, int64_t h0, int n, const int64_t (&v)[8],
+                                          int64_t begin, int E, int16_t* le) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int i = u * kGThreads + threadIdx.x;
+        const int64_t e = v[u] - begin;
+        if (i < n) le[i] = (int16_t)((e >= 0 && e < E) ? e : -1);
+    }
+    if (n > 8 * kGThreads) load_group_experts(ids, h0 + 8 * kGThreads, h0 + n, 0, begin, E, le + 8 * kGThreads);
+}
+
 __device__ __forceinline__ int smallest_in(const int16_t* le, int t_local, int k, int E) {
     int emin = E;
     for (int j = 0; j < k; ++j) {
@@ -597,7 +618,9 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     for (int i = tid; i < 2 * kGWaves * E; i += kGThreads) lds[i] = 0;
     const int tg0 = g * kRouteTokensPerGroup, tg1 = min(T, tg0 + kRouteTokensPerGroup);
-    load_group_experts(ids, (int64_t)tg0 * k, (int64_t)tg1 * k, k, expert_begin, E, le);
+    const int nh = (tg1 - tg0) * k;
+    int64_t idv[8];
+    fetch_ids(ids, (int64_t)tg0 * k, nh, idv);  // in flight during the group-count loads below
 
     // ---- scan of the group counts: totals and this group's bases per expert.  With E <= 256 the
     // threads split as (expert, slice of the groups), each summing every nsl-th group with several
@@ -679,6 +702,9 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int
     lds_barrier();
     if (g == 0)
         for (int e = tid; e <= E; e += kGThreads) p.offsets[e] = soff[e];
+
+    store_ids(ids, (int64_t)tg0 * k, nh, idv, expert_begin, E, le);
+    lds_barrier();
 
     // ---- this group's per-wave bases, then the stable scatter (as in route_scatter_kernel)
     const int t0 = min(tg1, tg0 + w * kWaveTokens);
