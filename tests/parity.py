@@ -117,3 +117,15 @@ def y_errors(y, ref):
 def assert_y_gate(y, ref, what=""):
     rel_max, rel_mean = y_errors(y, ref)
     assert rel_max <= 1e-2 and rel_mean <= 5e-3, f"{what}: y max err {rel_max:.3e}, mean rel err {rel_mean:.3e}"
+
+
+def tile_columns(which):
+    """Weight row (within a 256-row block) stored at each tile column of the tiled weight layout, as
+    documented for moe_prepare_weights in include/moe.h (which = 1: W1, 2: W2)."""
+    c = np.arange(256)
+    if which == 1:
+        G, b, j = c >> 6, (c >> 4) & 3, c & 15
+        ch = 32 * G + 2 * j + (b & 1)                  # SwiGLU channel; gate rows for b < 2, up rows for b >= 2
+        return (ch // 8) * 16 + (ch % 8) + 8 * (b >= 2)
+    S, b, j = c >> 7, (c >> 4) & 7, c & 15
+    return 128 * S + 8 * j + b

@@ -12,7 +12,7 @@ from moe_expert_ffn_plan_amd import binding as B
 from moe_expert_ffn_plan_amd import inputs
 from oracle.forward import dequant_fp4_rows, dequant_fp8_rows, forward_ref, forward_tokens
 from oracle.routing import plan_ref
-from parity import (assert_fp8_gate, assert_plan_equal, assert_y_gate, bf16_to_f32, gpu_plan_to_numpy,
+from parity import (tile_columns, assert_fp8_gate, assert_plan_equal, assert_y_gate, bf16_to_f32, gpu_plan_to_numpy,
                     linear1_cancellation)
 
 pytestmark = pytest.mark.gpu
@@ -123,22 +123,11 @@ def test_forward_tp_slice_full(gpu):
     check_full(w, {k: v.cpu() for k, v in d.items()}, out)
 
 
-def _tile_columns(which):
-    """Weight row (within a 256-row block) stored at each tile column, as documented in moe.h."""
-    c = np.arange(256)
-    if which == 1:
-        G, b, j = c >> 6, (c >> 4) & 3, c & 15
-        ch = 32 * G + 2 * j + (b & 1)                  # SwiGLU channel; gate rows for b < 2, up rows for b >= 2
-        return (ch // 8) * 16 + (ch % 8) + 8 * (b >= 2)
-    S, b, j = c >> 7, (c >> 4) & 7, c & 15
-    return 128 * S + 8 * j + b
-
-
 def _tile_reference(w, w_sf, N, K, which):
     """The documented tiled layout, built with NumPy index arithmetic."""
     E = w.shape[0]
     NT, KT = N // 256, K // 128
-    src = _tile_columns(which)
+    src = tile_columns(which)
     assert np.array_equal(np.sort(src), np.arange(256))
     p = np.arange(1024)
     c = p >> 2
