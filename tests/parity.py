@@ -12,8 +12,13 @@ Gates (one reading of the stated bars):
   BF16 input of the epilogue is not determined by the accumulation at all,
   since gfx950's scaled MFMA carries a dot-product error up to about
   2**-19 of the sum of |products| (measured), 32x below that threshold;
-* y (BF16): max |y - ref| <= 1e-2 * max |ref| and
-  sum |y - ref| / sum |ref| <= 5e-3.
+* y (BF16): max |y - ref| <= 1e-2 * max |ref| + a, and
+  sum |y - ref| / sum |ref| <= 5e-3, where a (per element of y) is how far the
+  FP8 differences admitted above can move it: Linear2 is linear in h, so an
+  admitted difference of at most fp8_flip_bound in h[r, c] moves slot row r
+  by at most that times |W2[:, c]|, and the combine adds a token's slot rows.
+  Without such differences a = 0.  (One admitted flip of an element that
+  dominates its row moves that token's y by a few percent of max |ref|.)
 """
 import numpy as np
 
@@ -114,8 +119,23 @@ def y_errors(y, ref):
     return rel_max, rel_mean
 
 
-def assert_y_gate(y, ref, what=""):
+def fp8_flip_bound(q_ref, sf_ref):
+    """Per element, an upper bound on the value difference the FP8 gate's 1-ulp clause admits, from the
+    oracle's (code, scale) alone: one ulp at up to twice the scale (a scale one step coarser) and up to the
+    next binade (the larger of the two magnitudes), i.e. 4 ulp of the oracle's value at its own scale."""
+    s = np.repeat(np.ldexp(1.0, np.asarray(sf_ref, np.int64) - 127), 32, axis=-1)
+    m = np.abs(fp8_values(q_ref, sf_ref)) / s
+    _, e = np.frexp(np.maximum(m, 1e-300))
+    return 4.0 * np.ldexp(1.0, np.maximum(e - 1, -6) - 3) * s
+
+
+def assert_y_gate(y, ref, what="", allowance=None):
+    """The y gate above; `allowance` is a (per element of y, from the admitted FP8 differences)."""
     rel_max, rel_mean = y_errors(y, ref)
+    if allowance is not None:
+        m = float(np.abs(ref).max()) if ref.size else 0.0
+        over = np.abs(np.asarray(y, np.float64) - ref) - allowance
+        rel_max = float(max(over.max(), 0.0)) / m if m > 0 else float(max(over.max(), 0.0))
     assert rel_max <= 1e-2 and rel_mean <= 5e-3, f"{what}: y max err {rel_max:.3e}, mean rel err {rel_mean:.3e}"
 
 

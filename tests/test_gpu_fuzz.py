@@ -21,7 +21,7 @@ from test_gpu_forward import check_full, run_gpu
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 24
+N_CASES = 120
 
 
 def fuzz_case(i):

@@ -2,7 +2,8 @@
 import numpy as np
 
 from oracle import formats as F
-from parity import assert_fp8_gate, e4m3_step_distance, fp8_ulp_distance, fp8_values, y_errors
+from parity import (assert_fp8_gate, assert_y_gate, e4m3_step_distance, fp8_flip_bound, fp8_ulp_distance,
+                    fp8_values, y_errors)
 
 
 def test_fp8_values_match_oracle_decode():
@@ -61,3 +62,38 @@ def test_y_errors():
     assert y_errors(ref, ref) == (0.0, 0.0)
     mx, mean = y_errors(ref + np.array([0.04, 0, 0], np.float32), ref)
     assert abs(mx - 0.01) < 1e-7 and abs(mean - 0.04 / 7) < 1e-7
+
+
+def test_flip_bound_covers_every_admitted_difference():
+    # brute force: every finite E4M3 code of the oracle at scale 2^0, every device code at the same scale or
+    # one step coarser or finer; wherever the 1-ulp clause admits the pair, the difference is within the bound
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    qr, qg = np.meshgrid(codes, codes, indexing="ij")
+    qr = np.repeat(qr.reshape(-1, 1), 32, axis=1)
+    qg = np.repeat(qg.reshape(-1, 1), 32, axis=1)
+    sr = np.full((qr.shape[0], 1), 127, np.uint8)
+    checked = 0
+    for dsf in (-1, 0, 1):
+        sg = (sr.astype(int) + dsf).astype(np.uint8)
+        ok = fp8_ulp_distance(qg, sg, qr, sr) <= 1.0
+        diff = np.abs(fp8_values(qg, sg) - fp8_values(qr, sr))
+        assert np.all(diff[ok] <= fp8_flip_bound(qr, sr)[ok])
+        checked += int(ok.sum())
+    assert checked > 0
+
+
+def test_y_gate_allowance_admits_only_the_propagated_amount():
+    ref = np.full((10, 100), 100.0)
+    y = ref.copy()
+    y[3, 7] += 3.0                                  # 3% of max |ref| at one element; mean error stays tiny
+    allow_here = np.zeros_like(ref)
+    allow_here[3, 7] = 2.5                          # leaves 0.5% of max |ref|
+    allow_elsewhere = np.full_like(ref, 5.0)
+    allow_elsewhere[3, 7] = 0.0
+    for allowance, passes in ((None, False), (allow_here, True), (allow_elsewhere, False)):
+        try:
+            assert_y_gate(y, ref, "case", allowance=allowance)
+            ok = True
+        except AssertionError:
+            ok = False
+        assert ok == passes
