@@ -661,11 +661,10 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
 // Both groups pass the same S barriers; group 1 multiplies stage S - 1
 // after the last one.  Group 1 runs the epilogue of a tile right after its
 // last MFMAs of that tile (half a step after group 0, overlapping group 0's
-// next issue, reads and MFMAs).  Group 0 runs a Linear1 epilogue (VALU-
-// bound) right after its last MFMAs too, but a Linear2 epilogue (store-
-// bound) after the next barrier, before its next MFMAs: its stores then
-// overlap group 1's MFMAs instead of holding group 1 at the barrier
-// (measured: Linear2 1-1.3% faster).
+// next issue, reads and MFMAs).  Group 0 runs it after the next barrier,
+// before its next MFMAs, so it overlaps group 1's MFMAs instead of holding
+// group 1 at the barrier (measured: Linear2 1-1.3% and Linear1 ~1%
+// faster).
 //
 // Per-tile tables reach LDS through the same DMA stream, a fixed number of
 // extra instructions per wave per stage so the vmcnt arithmetic stays exact:
@@ -831,19 +830,19 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
 #pragma unroll
         for (int s = 0; s < L::NS - 1; ++s)
             if (s < S) issue(s);
-        // Linear2: the epilogue of a finished tile runs after the next barrier (its stores then overlap
-        // group 1's MFMAs instead of holding group 1 at the barrier), before this group's next MFMAs
+        // the epilogue of a finished tile runs after the next barrier (it then overlaps group 1's MFMAs
+        // instead of holding group 1 at the barrier), before this group's next MFMAs
         bool pending = false;
         TileId pt;
         int pci = 0;
         auto deferred_epilogue = [&]() {
-            if constexpr (!L1) {
-                if (pending)
-                    epilogue<BM, C::MI, C::NI, L1, PARTIAL, FUSED, EPI>(acc, g, pt, wrow0, pt.n * 512 + wcol0,
-                                                                   sh.wts[pci % kTableSlots],
-                                                                   sh.meta[pci % kTableSlots], lane);
-                pending = false;
+            if (pending) {
+                epilogue<BM, C::MI, C::NI, L1, PARTIAL, FUSED, EPI>(acc, g, pt, wrow0, pt.n * 512 + wcol0,
+                                                               sh.wts[pci % kTableSlots],
+                                                               sh.meta[pci % kTableSlots], lane);
+                if constexpr (FUSED && L1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // stores complete
             }
+            pending = false;
         };
         for (int gs = 0, kt = 0, ci = 0; gs < S; ++gs) {
             wait_stages_and_barrier<C::D0>(min(L::NS - 2, S - 1 - gs));  // B_gs
@@ -854,16 +853,9 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
             read_frags<BM, 512>(f, sh.smem + (gs % L::NS) * L::STAGE, wrow0, wcol0, lane);
             mfma_step(acc, f, kt == 0);
             if (++kt == KT) {
-                if constexpr (L1) {
-                    epilogue<BM, C::MI, C::NI, L1, PARTIAL, FUSED, EPI>(acc, g, ct, wrow0, ct.n * 512 + wcol0,
-                                                                   sh.wts[ci % kTableSlots],
-                                                                   sh.meta[ci % kTableSlots], lane);
-                    if constexpr (FUSED) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // stores complete
-                } else {
-                    pending = true;
-                    pt = ct;
-                    pci = ci;
-                }
+                pending = true;
+                pt = ct;
+                pci = ci;
                 kt = 0;
                 ++ci;
             }
