@@ -42,9 +42,9 @@
 //    were two-way conflicted).
 //  * 512-column tiles run 8 waves as two groups of four that alternate
 //    ("ping-pong"): while one group issues the MFMAs of its K-step, the other
-//    reads its next fragments from LDS and issues its share of the DMA, and
-//    every phase change is a workgroup barrier.  The two waves sharing a
-//    SIMD are thus never both waiting on LDS, which a single group of
+//    issues its share of the DMA and reads its next fragments from LDS, with
+//    one workgroup barrier per K-step.  The two waves sharing a SIMD are
+//    thus rarely both away from the matrix core, which a single group of
 //    barrier-synchronised waves cannot avoid.  Group 0 streams most of the
 //    weights, group 1 the activation rows and the rest of the weights.
 //    256-column tiles (small N) use one group of four waves that reads, then
