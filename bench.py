@@ -1,7 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the fused MoE expert FFN hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload tp_slice]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload skewed]
+
+The default workload is skewed (16,384 tokens, hidden 7168, intermediate 2048, 32 local experts of
+256, Zipf(1.2) top-8 routing, 10% of the rows of x scaled by 50): the largest of the configurations
+that fits one GPU, the one the headline number is quoted on.
 
 One step = the whole hot path on one batch of synthetic input already resident
 in HBM: routing tables (moe_plan), grouped Linear1 with the fused
@@ -91,14 +95,23 @@ def cpu_baseline(w, d_gpu, sample_tokens: int, min_seconds: float = 10.0):
         dt += time.perf_counter() - t0
         reps += 1
     flops = 2.0 * len(hits) * 3 * w.hidden * w.intermediate * reps
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) or 1
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        cores = max(int(i.get("num_threads", 1)) for i in pools) or 1
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer', '')}, "
+                         f"{i.get('num_threads')} threads)" for i in pools)
     except Exception:
         cores = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except Exception:
+        affinity = None
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"first {toks.size} of {w.num_tokens} tokens ({len(hits)} local top-k rows), whole oracle "
-                      f"forward incl. weight dequantisation, {reps} run(s), {dt:.1f} s"}
+                      f"forward incl. weight dequantisation, {reps} run(s), {dt:.1f} s",
+            "cpu_count": os.cpu_count(), "affinity_cpus": affinity, "blas": blas}
 
 
 def main() -> int:
@@ -106,7 +119,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="tp_slice")
+    ap.add_argument("--workload", default="skewed")
     ap.add_argument("--weight-copies", type=int, default=3)
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -128,7 +141,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs one GPU's share of the MoE layer; --gpus {args.gpus} is not supported "
-              f"(the multi-GPU sharding is described in DESIGN.md, not built)", file=sys.stderr)
+              f"(only one GPU's share is built: no sharding across GPUs, no collectives)", file=sys.stderr)
         return 2
 
     import torch
@@ -211,6 +224,15 @@ def main() -> int:
     ids = d["topk_idx"]
     hit_tokens = int(((ids >= 0) & (ids < w.num_experts)).any(dim=1).sum().item())
 
+    # the workspace's status word reports a single-launch GEMM that gave up waiting (y is then NaN)
+    status = B.forward_view(s, ws)["sync_status"]
+
+    def check_status(what):
+        torch.cuda.synchronize()
+        if int(status.item()) != 0 or not bool(torch.isfinite(y.float()).all()):
+            raise RuntimeError(f"bench.py: {what}: a GEMM launch gave up waiting or y is not finite")
+    check_status("warmup")
+
     # timed steps: wall time; HIP events bracket only the dominant GEMM launch (same stream)
     k_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     if args.graph:
@@ -245,6 +267,7 @@ def main() -> int:
         t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
     k_ms = sum(e[0].elapsed_time(e[1]) for e in k_evs) / args.steps
+    check_status("timed steps")
 
     # untimed breakdown passes: an event between every stage (and the two-launch path for comparison)
     def breakdown(staged):

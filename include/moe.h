@@ -25,8 +25,10 @@
  *    workspace.  Call once eagerly before capturing (the first call on a
  *    device queries its properties).
  *  - Validation happens on the host before anything is enqueued, in this
- *    order: NULL shape/pointers (MOE_ERR_NULL), shape limits (MOE_ERR_SHAPE),
- *    alignment (MOE_ERR_ALIGN), workspace size (MOE_ERR_WORKSPACE), device
+ *    order: NULL shape (MOE_ERR_NULL), shape limits (MOE_ERR_SHAPE), the
+ *    declared weight layout of the calls that read weights
+ *    (MOE_ERR_LAYOUT), NULL pointers (MOE_ERR_NULL), alignment
+ *    (MOE_ERR_ALIGN), workspace size (MOE_ERR_WORKSPACE), device
  *    architecture (MOE_ERR_ARCH).  A failed kernel launch returns
  *    MOE_ERR_HIP.  num_tokens == 0 is a no-op returning MOE_OK.
  *  - Expert ids outside [expert_begin, expert_begin + num_experts) are not
@@ -56,7 +58,14 @@ enum moe_status {
     MOE_ERR_ALIGN = -3,
     MOE_ERR_WORKSPACE = -4,
     MOE_ERR_ARCH = -5,
-    MOE_ERR_HIP = -6
+    MOE_ERR_HIP = -6,
+    MOE_ERR_LAYOUT = -7
+};
+
+/* Layout of the expert weights a call is given (moe_shape.weight_layout). */
+enum moe_weight_layout {
+    MOE_WEIGHTS_PLAIN = 0,  /* row-major as drawn: see "plain" under moe_forward */
+    MOE_WEIGHTS_TILED = 1   /* the output of moe_prepare_weights */
 };
 
 /* Problem shape.  Limits (else MOE_ERR_SHAPE, or MOE_ERR_ALIGN for the
@@ -81,6 +90,15 @@ enum moe_status {
  *                hardware exp2 and reciprocal (the default; the pages'
  *                fast-math path).  1: g / (1 + expf(-g)) with the accurate
  *                library expf and IEEE division.
+ * Weight layout:
+ *   weight_layout  MOE_WEIGHTS_PLAIN or MOE_WEIGHTS_TILED (else
+ *                MOE_ERR_SHAPE): the layout of the w1/w1_sf/w2/w2_sf the
+ *                call is given.  The calls that read weights
+ *                (moe_forward, moe_linear1, moe_linear2, moe_expert_ffn)
+ *                take only MOE_WEIGHTS_TILED and return MOE_ERR_LAYOUT for
+ *                MOE_WEIGHTS_PLAIN (so a zero-initialised shape is refused
+ *                there until the caller states that it ran
+ *                moe_prepare_weights); the other calls ignore the field.
  */
 typedef struct moe_shape {
     int32_t num_tokens;
@@ -92,6 +110,7 @@ typedef struct moe_shape {
     int32_t block_m;
     float swiglu_limit;
     int32_t exact_silu;
+    int32_t weight_layout;
 } moe_shape;
 
 /* Worst-case padded row count of the routing layout ("pool capacity"):
@@ -182,7 +201,9 @@ MOE_API int moe_plan_view_get(const moe_shape* shape, void* plan_ws, moe_plan_vi
  *                                epilogue, walk-through section 4.6)
  *   w1, w1_sf, w2, w2_sf         the expert weights in the TILED layout made
  *                                once by moe_prepare_weights (below) from the
- *                                plain layout:
+ *                                plain layout; the shape must say so
+ *                                (weight_layout = MOE_WEIGHTS_TILED), else
+ *                                the call returns MOE_ERR_LAYOUT:
  *     plain w1    uint8 [E, 2I, H/2]  FP4 E2M1 pairs, even K in the low
  *                                     nibble; rows interleave gate/up by 8:
  *                                     [g0..7, u0..7, g8..15, u8..15, ...]
@@ -196,9 +217,12 @@ MOE_API int moe_plan_view_get(const moe_shape* shape, void* plan_ws, moe_plan_vi
  *                                Linear2 rows; +0 for a token with none.
  * plan_ws: tables built by moe_plan for the same topk_idx and shape, or
  *   NULL to build them inside ws as part of this call.
- * ws: workspace of >= moe_forward_workspace_bytes, 256-byte aligned; holds
- *   the FP8 Linear2 input (and its scales) and the BF16 per-slot Linear2
- *   rows between kernels. */
+ * ws: workspace of >= moe_forward_workspace_bytes, 256-byte aligned, any
+ *   initial contents; holds the FP8 Linear2 input (and its scales), the BF16
+ *   per-slot Linear2 rows between kernels, and the single launch's
+ *   completion flags, launch counter and status word (see moe_expert_ffn).
+ *   If the GEMMs ran as one launch and a Linear2 tile gave up waiting
+ *   (see moe_expert_ffn), every element of y is NaN. */
 MOE_API int moe_forward_workspace_bytes(const moe_shape* shape, size_t* bytes);
 
 /* One-time weight re-layout (the analog of the pages' weight transform,
@@ -242,14 +266,16 @@ MOE_API int moe_forward(const moe_shape* shape,
  * kernel tail and ramp; with many it measured slightly slower.)  They are
  * exposed so a caller can schedule or time the stages itself.  Arguments mean what they mean for moe_forward; plan_ws
  * (from moe_plan) is required here, and ws must be the same forward
- * workspace for all of them.
+ * workspace for all of them.  moe_linear1 clears the workspace's status word
+ * (nothing in the two-launch schedule sets it).
  *   moe_linear1: grouped Linear1 over the routing layout with the fused
  *     SwiGLU x top-k weight and FP8 requant epilogue -> h_q, h_sf in ws
  *     (reading notes "stage three" and "stage four").
  *   moe_linear2: grouped Linear2 of h_q with BF16 output -> yslot in ws
  *     ("stage five").
  *   moe_combine: y[t] = BF16(FP32 sum over j of yslot[slot[t, j]])
- *     ("stage six"; walk-through section 4.6 "combine reduction"). */
+ *     ("stage six"; walk-through section 4.6 "combine reduction"); NaN in
+ *     every element of y instead when the status word is non-zero. */
 MOE_API int moe_linear1(const moe_shape* shape,
                 const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
                 const uint8_t* w1, const uint8_t* w1_sf,
@@ -268,13 +294,18 @@ MOE_API int moe_combine(const moe_shape* shape, const void* plan_ws,
  * Used when 2I and H are multiples of 512, both K-loops are long enough for
  * the persistent kernel (H/128 and I/128 >= 4 for block_m >= 32, >= 6 for
  * block_m 16) and 2I/512 <= 64; otherwise this is moe_linear1 + moe_linear2.
- * The completion flags live in ws (any initial contents: each launch stamps
- * them with a fresh epoch); calls sharing a ws must not overlap.  A Linear2
- * tile that waits for about half a second gives up and sets the forward view's
- * sync_status to 1 (it needs every workgroup of the launch resident at once;
- * the library never clears the word).  When `stream` is being captured, a
- * one-thread kernel that advances an epoch word in ws is recorded ahead of
- * the launch, so every replay of the graph stamps fresh flags. */
+ * The completion flags live in ws (any initial contents).  Ahead of every
+ * single launch, eager or recorded into a graph, a one-thread kernel
+ * advances a launch counter in ws and clears the status word; the launch
+ * stamps its flags with a value derived one-to-one from the counter, so no
+ * two of 2^32 successive launches on one workspace stamp the same value and
+ * a flag left by an earlier launch never reads as set.  Calls sharing a ws
+ * must not overlap.  A Linear2 tile that waits for about half a second
+ * gives up, sets the forward view's sync_status to 1 and computes on rows
+ * that may be unfinished (the launch needs every workgroup resident at
+ * once, e.g. no other kernel occupying compute units); moe_combine then
+ * writes NaN over all of y.  The word reports on the latest GEMM launch on
+ * the workspace: the single launch clears it first, moe_linear1 clears it. */
 MOE_API int moe_expert_ffn(const moe_shape* shape,
                 const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
                 const uint8_t* w1, const uint8_t* w1_sf,
@@ -289,8 +320,9 @@ MOE_API int moe_expert_ffn(const moe_shape* shape,
  *         [r / block_m][g / 4][r % block_m][g % 4]
  *   yslot uint16 [cap, H]     BF16 Linear2 output per slot row
  *   plan  the plan region used when moe_forward got plan_ws == NULL
- *   sync_status  uint32 word set to 1 when a moe_expert_ffn launch gave up
- *         waiting (see there)
+ *   sync_status  uint32 word: 1 if the latest single-launch GEMM on this
+ *         workspace gave up waiting (see moe_expert_ffn), else 0 once any
+ *         GEMM has run on the workspace
  * Rows of padding (and rows >= R_pad) hold unspecified values. */
 typedef struct moe_forward_view {
     uint8_t* h_q;

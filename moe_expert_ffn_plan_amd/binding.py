@@ -15,7 +15,10 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
 STATUS = {0: "ok", -1: "null pointer", -2: "unsupported shape", -3: "misaligned pointer or dimension",
-          -4: "workspace too small", -5: "device is not gfx950", -6: "HIP runtime error"}
+          -4: "workspace too small", -5: "device is not gfx950", -6: "HIP runtime error",
+          -7: "weights not declared in the tiled layout"}
+
+WEIGHTS_PLAIN, WEIGHTS_TILED = 0, 1   # moe_shape.weight_layout
 
 
 class MoeError(RuntimeError):
@@ -27,7 +30,8 @@ class MoeError(RuntimeError):
 class MoeShape(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32), ("intermediate", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("expert_begin", ctypes.c_int32), ("topk", ctypes.c_int32),
-                ("block_m", ctypes.c_int32), ("swiglu_limit", ctypes.c_float), ("exact_silu", ctypes.c_int32)]
+                ("block_m", ctypes.c_int32), ("swiglu_limit", ctypes.c_float), ("exact_silu", ctypes.c_int32),
+                ("weight_layout", ctypes.c_int32)]
 
 
 class PlanView(ctypes.Structure):
@@ -83,15 +87,18 @@ def lib() -> ctypes.CDLL:
 
 
 def make_shape(num_tokens, hidden, intermediate, num_experts, topk, block_m, expert_begin=0, swiglu_limit=0.0,
-               exact_silu=False) -> MoeShape:
+               exact_silu=False, weight_layout=WEIGHTS_TILED) -> MoeShape:
+    """A moe_shape.  weight_layout states the layout of the weights the call is given: the Python side
+    always passes the tiled weights prepare_weights returns, hence the default."""
     return MoeShape(num_tokens, hidden, intermediate, num_experts, expert_begin, topk, block_m, float(swiglu_limit),
-                    int(bool(exact_silu)))
+                    int(bool(exact_silu)), int(weight_layout))
 
 
-def shape_of(workload, num_tokens=None, expert_begin=0, swiglu_limit=0.0, exact_silu=False) -> MoeShape:
+def shape_of(workload, num_tokens=None, expert_begin=0, swiglu_limit=0.0, exact_silu=False,
+             weight_layout=WEIGHTS_TILED) -> MoeShape:
     w = workload
     return make_shape(w.num_tokens if num_tokens is None else num_tokens, w.hidden, w.intermediate,
-                      w.num_experts, w.topk, w.block_m, expert_begin, swiglu_limit, exact_silu)
+                      w.num_experts, w.topk, w.block_m, expert_begin, swiglu_limit, exact_silu, weight_layout)
 
 
 def _check(fn, status):

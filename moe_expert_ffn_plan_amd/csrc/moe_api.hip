@@ -33,6 +33,7 @@ int check_shape(const moe_shape* s) {
     if ((int64_t)s->num_tokens * s->topk >= (1ll << 30)) return MOE_ERR_SHAPE;
     if (!(s->swiglu_limit >= 0.0f && s->swiglu_limit <= 3.0e38f)) return MOE_ERR_SHAPE;  // also rejects NaN
     if (s->exact_silu != 0 && s->exact_silu != 1) return MOE_ERR_SHAPE;
+    if (s->weight_layout != MOE_WEIGHTS_PLAIN && s->weight_layout != MOE_WEIGHTS_TILED) return MOE_ERR_SHAPE;
     if (s->hidden > (1 << 20) || s->intermediate > (1 << 20)) return MOE_ERR_SHAPE;
     if (s->hidden % 256 != 0 || s->intermediate % 128 != 0) return MOE_ERR_ALIGN;
     // kernels address each operand's rows with 32-bit offsets
@@ -41,6 +42,13 @@ int check_shape(const moe_shape* s) {
     if (capacity_rows(*s) * s->intermediate >= lim) return MOE_ERR_SHAPE;
     if ((int64_t)s->hidden * s->intermediate >= lim) return MOE_ERR_SHAPE;
     return MOE_OK;
+}
+
+// The calls that read weights: a valid shape that also declares the tiled layout.
+int check_weight_shape(const moe_shape* s) {
+    const int st = check_shape(s);
+    if (st != MOE_OK) return st;
+    return s->weight_layout == MOE_WEIGHTS_TILED ? MOE_OK : MOE_ERR_LAYOUT;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -72,6 +80,7 @@ const char* moe_status_str(int status) {
         case MOE_ERR_WORKSPACE: return "workspace too small";
         case MOE_ERR_ARCH: return "device is not gfx950";
         case MOE_ERR_HIP: return "HIP runtime error";
+        case MOE_ERR_LAYOUT: return "weights not declared in the tiled layout";
         default: return "unknown status";
     }
 }
@@ -186,7 +195,7 @@ int moe_prepare_weights(const moe_shape* shape, int which, const uint8_t* w, con
 int moe_linear1(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
                 const uint8_t* w1, const uint8_t* w1_sf, const void* plan_ws, void* ws, size_t ws_bytes,
                 void* stream) {
-    int st = check_shape(shape);
+    int st = check_weight_shape(shape);
     if (st != MOE_OK) return st;
     if (shape->num_tokens == 0) return MOE_OK;
     if (!x || !x_sf || !topk_w || !w1 || !w1_sf || !plan_ws || !ws) return MOE_ERR_NULL;
@@ -200,13 +209,14 @@ int moe_linear1(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, c
     char* base = static_cast<char*>(ws);
     const GemmProblem g{shape, &p, F.plan.cap};
     const hipError_t e = launch_linear1(g, x, x_sf, topk_w, w1, w1_sf, reinterpret_cast<uint8_t*>(base + F.h_q),
-                                        reinterpret_cast<uint8_t*>(base + F.h_sf), static_cast<hipStream_t>(stream));
+                                        reinterpret_cast<uint8_t*>(base + F.h_sf),
+                                        reinterpret_cast<uint32_t*>(base + F.status), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int moe_linear2(const moe_shape* shape, const uint8_t* w2, const uint8_t* w2_sf, const void* plan_ws, void* ws,
                 size_t ws_bytes, void* stream) {
-    int st = check_shape(shape);
+    int st = check_weight_shape(shape);
     if (st != MOE_OK) return st;
     if (shape->num_tokens == 0) return MOE_OK;
     if (!w2 || !w2_sf || !plan_ws || !ws) return MOE_ERR_NULL;
@@ -227,7 +237,7 @@ int moe_linear2(const moe_shape* shape, const uint8_t* w2, const uint8_t* w2_sf,
 int moe_expert_ffn(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
                    const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2, const uint8_t* w2_sf,
                    const void* plan_ws, void* ws, size_t ws_bytes, void* stream) {
-    int st = check_shape(shape);
+    int st = check_weight_shape(shape);
     if (st != MOE_OK) return st;
     if (shape->num_tokens == 0) return MOE_OK;
     if (!x || !x_sf || !topk_w || !w1 || !w1_sf || !w2 || !w2_sf || !plan_ws || !ws) return MOE_ERR_NULL;
@@ -260,7 +270,8 @@ int moe_combine(const moe_shape* shape, const void* plan_ws, const void* ws, siz
     if ((st = check_arch_current()) != MOE_OK) return st;
     const PlanPtrs p = plan_ptrs(F.plan, const_cast<void*>(plan_ws));
     const char* base = static_cast<const char*>(ws);
-    const hipError_t e = launch_combine(*shape, reinterpret_cast<const uint16_t*>(base + F.yslot), p.slot, y,
+    const hipError_t e = launch_combine(*shape, reinterpret_cast<const uint16_t*>(base + F.yslot), p.slot,
+                                        reinterpret_cast<const uint32_t*>(base + F.status), y,
                                         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
@@ -269,7 +280,7 @@ int moe_forward(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, c
                 const float* topk_w, const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2,
                 const uint8_t* w2_sf, uint16_t* y, const void* plan_ws, void* ws, size_t ws_bytes,
                 void* stream) {
-    int st = check_shape(shape);
+    int st = check_weight_shape(shape);
     if (st != MOE_OK) return st;
     if (shape->num_tokens == 0) return MOE_OK;
     if (!x || !x_sf || !topk_idx || !topk_w || !w1 || !w1_sf || !w2 || !w2_sf || !y || !ws) return MOE_ERR_NULL;

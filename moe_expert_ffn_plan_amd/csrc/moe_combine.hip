@@ -2,7 +2,8 @@
 // with the sum in FP32 and tokens without a local hit written as +0
 // (walk-through section 4.6 "combine reduction"; reading notes "stage six").
 // The routing weight was applied in the Linear1 epilogue, so the sum is
-// unweighted.
+// unweighted.  If the forward's status word reports that a single-launch GEMM gave up waiting for
+// its Linear1 rows (so some slot rows may be wrong), every element of y is written as NaN instead.
 //
 // HBM-bound: each thread owns 8 consecutive BF16 columns of one token at a time (one 16-byte load per
 // slot), a workgroup 256 such spans of one token (blockIdx.x = token, blockIdx.y = first span block),
@@ -23,11 +24,20 @@ constexpr int kMaxBlocks = 32768;
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
+constexpr uint32_t kNaNPair = 0x7FC07FC0u;  // two BF16 quiet NaNs
+
 __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __restrict__ yslot,
                                                            const int32_t* __restrict__ slot, int k, int H,
+                                                           const uint32_t* __restrict__ status,
                                                            uint16_t* __restrict__ y) {
     const int t = blockIdx.x;
     const int32_t* s = slot + (size_t)t * k;
+    if (__builtin_amdgcn_readfirstlane(*status) != 0u) {
+        const v4i nan = v4i{(int)kNaNPair, (int)kNaNPair, (int)kNaNPair, (int)kNaNPair};
+        for (int c = blockIdx.y * kThreads + threadIdx.x; c < H / 8; c += gridDim.y * kThreads)
+            *reinterpret_cast<v4i*>(y + (size_t)t * H + c * 8) = nan;
+        return;
+    }
     for (int c = blockIdx.y * kThreads + threadIdx.x; c < H / 8; c += gridDim.y * kThreads) {  // 8-column span
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int j0 = 0; j0 < k; j0 += kBatch) {
@@ -64,12 +74,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
 
 }  // namespace
 
-hipError_t launch_combine(const moe_shape& s, const uint16_t* yslot, const int32_t* slot, uint16_t* y,
-                          hipStream_t stream) {
+hipError_t launch_combine(const moe_shape& s, const uint16_t* yslot, const int32_t* slot, const uint32_t* status,
+                          uint16_t* y, hipStream_t stream) {
     if (s.num_tokens == 0) return hipSuccess;
     const int blocks = (s.hidden / 8 + kThreads - 1) / kThreads;  // span blocks per token
     const dim3 grid((unsigned)s.num_tokens, (unsigned)std::max(1, std::min(blocks, kMaxBlocks / s.num_tokens)));
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, stream, yslot, slot, s.topk, s.hidden, y);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, stream, yslot, slot, s.topk, s.hidden, status, y);
     return hipGetLastError();
 }
 

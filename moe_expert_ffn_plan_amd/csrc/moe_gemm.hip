@@ -59,7 +59,6 @@
 
 #include <algorithm>
 #include <atomic>
-#include <random>
 
 namespace moe {
 namespace {
@@ -91,6 +90,7 @@ struct GemmArgs {
     float swiglu_limit;     // Linear1: > 0 clamps gate from above and up on both sides before SwiGLU
     int exact_silu;         // Linear1: 1 = accurate expf and IEEE division in SiLU
     int count_idx;          // scalars[count_idx] = tiles in the list
+    uint32_t* status;       // Linear1 launched on its own: the forward's status word, cleared by workgroup 0
 };
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -605,6 +605,7 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
     __shared__ float row_w[BM];
     __shared__ int row_tok[BM];
 
+    if (L1 && g.status && blockIdx.x == 0 && threadIdx.x == 0) *g.status = 0u;
     TileId t;
     if (!tile_of_block(g, 256, t)) return;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -696,7 +697,16 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
 // resident: every awaited tile is being computed.  A Linear2 tile reads only
 // rows whose Linear1 tiles are done and no XCD reads those lines earlier in
 // the launch, so plain loads see the stored values.  After kGateSpins polls
-// the wait gives up and sets the status word instead of hanging.
+// the wait gives up and sets the status word instead of hanging (the tile
+// then computes on rows that may be unfinished, and the combine, which reads
+// the word, writes NaN over all of y).
+//
+// The epoch is the value of a per-workspace counter that a one-thread kernel
+// advances ahead of every fused launch, eager or recorded into a graph, and
+// that nothing writes during the launch; successive launches on one
+// workspace therefore stamp distinct values for 2^32 launches.  It is passed
+// through a fixed bijection so that a workspace filled with one byte value
+// (counter and flags alike) does not start with matching flags.
 template <int BM, bool L1, bool FUSED>
 struct CfgPP {
     using L = StageLayout<BM, 512>;
@@ -977,6 +987,7 @@ __device__ __forceinline__ TileSeq round_robin(int begin, int end, int slot, int
 template <int BM, bool L1, bool PARTIAL, int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
     __shared__ PPShared<BM> sh;
+    if (L1 && g.status && blockIdx.x == 0 && threadIdx.x == 0) *g.status = 0u;
     int begin, end;
     xcd_chunk(g, g.N / 512, blockIdx.x % kNumXcd, begin, end);
     const TileSeq seq = round_robin(begin, end, blockIdx.x / kNumXcd, gridDim.x / kNumXcd);
@@ -986,18 +997,24 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
 
 struct FusedArgs {
     GemmArgs g1, g2;  // Linear1, Linear2
-    FusedSync sync;
-    // launches recorded into a graph: a word the preceding epoch_bump_kernel advanced, mixed into
-    // sync.epoch (whose host value is frozen at capture) so that each replay stamps fresh flags
+    FusedSync sync;   // sync.epoch is set on the device from epoch_word
+    // the workspace's launch counter, advanced by fused_prepare_kernel ahead of this launch
     const uint32_t* epoch_word;
 };
 
-// Advances the device epoch word of a forward workspace (one thread; runs before every recorded
-// single-launch GEMM).
-__global__ void epoch_bump_kernel(uint32_t* word) {
+// Flag value of the launch whose counter value is w: an odd-multiplier bijection of the 32-bit counter
+// (distinct counters give distinct values) followed by a constant xor, so that a counter and flags
+// holding the same fill pattern do not match (0x00.., 0x5A.., 0xAB.., 0xFF.. were checked).
+__device__ __forceinline__ uint32_t flag_value(uint32_t w) { return (w * 0x9E3779B1u) ^ 0x6C8E9CF5u; }
+
+// Runs (one thread) ahead of every fused launch on the same stream: advances the workspace's launch
+// counter, so that the launch stamps flags no earlier launch on the workspace stamped, and clears the
+// status word, which then reports on this launch only.
+__global__ void fused_prepare_kernel(uint32_t* epoch_word, uint32_t* status) {
     if (threadIdx.x == 0) {
-        const uint32_t v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(word, v + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t v = __hip_atomic_load(epoch_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(epoch_word, v + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -1012,10 +1029,9 @@ __global__ __launch_bounds__(512, 1) void gemm_fused_kernel(FusedArgs fa) {
     __shared__ PPShared<BM> sh;
     const int nslots = gridDim.x / kNumXcd, xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
     FusedSync sync = fa.sync;
-    if (fa.epoch_word) {  // every workgroup reads the same value: nothing in this launch writes the word
-        const uint32_t e = sync.epoch ^ __hip_atomic_load(fa.epoch_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sync.epoch = __builtin_amdgcn_readfirstlane(e != 0u ? e : 0x9E3779B9u);
-    }
+    // every workgroup reads the same counter value: nothing in this launch writes the word
+    sync.epoch = __builtin_amdgcn_readfirstlane(
+        flag_value(__hip_atomic_load(fa.epoch_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
     int b1, e1, b2, e2;
     xcd_chunk(fa.g1, fa.g1.N / 512, xcd, b1, e1);
     xcd_chunk(fa.g2, fa.g2.N / 512, xcd, b2, e2);
@@ -1141,8 +1157,9 @@ GemmArgs common_args(const GemmProblem& p) {
 }
 
 GemmArgs linear1_args(const GemmProblem& p, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
-                      const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf) {
+                      const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf, uint32_t* status) {
     GemmArgs a = common_args(p);
+    a.status = status;
     a.tiles = p.plan->tiles1;
     a.count_idx = 4;
     a.topk_w = topk_w;
@@ -1161,18 +1178,6 @@ GemmArgs linear2_args(const GemmProblem& p, const uint8_t* h_q, const uint8_t* h
     a.out_q = nullptr; a.out_sf = nullptr; a.out_bf16 = yslot;
     a.K = p.shape->intermediate; a.N = p.shape->hidden;
     return a;
-}
-
-// Epoch of a fused launch: a fresh value per launch, never 0, from a random start so that flag words
-// left in a workspace by an earlier process or launch do not match.
-uint32_t next_epoch() {
-    static std::atomic<uint32_t> counter{[] {
-        std::random_device rd;
-        return (uint32_t)rd();
-    }()};
-    uint32_t e;
-    do e = counter.fetch_add(1, std::memory_order_relaxed); while (e == 0);
-    return e;
 }
 
 }  // namespace
@@ -1199,30 +1204,27 @@ hipError_t launch_expert_ffn(const GemmProblem& p, const uint8_t* x, const uint8
                              const uint8_t* w2, const uint8_t* w2_sf, uint16_t* yslot, uint32_t* flags,
                              uint32_t* status, uint32_t* epoch_word, hipStream_t stream) {
     FusedArgs fa{};
-    fa.g1 = linear1_args(p, x, x_sf, topk_w, w1, w1_sf, h_q, h_sf);
+    fa.g1 = linear1_args(p, x, x_sf, topk_w, w1, w1_sf, h_q, h_sf, status);
     fa.g2 = linear2_args(p, h_q, h_sf, w2, w2_sf, yslot);
     if (!fused_supported(*p.shape)) {
         hipError_t e = launch_gemm<true>(p, fa.g1, stream);
         if (e != hipSuccess) return e;
         return launch_gemm<false>(p, fa.g2, stream);
     }
+    fa.g1.status = nullptr;  // fused_prepare_kernel clears the word
     fa.sync.flags = flags;
     fa.sync.status = status;
-    fa.sync.epoch = next_epoch();
     fa.sync.nt1 = fa.g1.N / 512;
+    fa.epoch_word = epoch_word;
     const int64_t tiles = std::max(one_tile_grid(p, fa.g1.N), one_tile_grid(p, fa.g2.N));
     if (tiles == 0) return hipSuccess;
     const dim3 grid((unsigned)persistent_grid(tiles)), block(512);
     const int bm = p.shape->block_m, bmg = gemm_bm(bm);
     const int epi = epi_of(fa.g1);
-    // a launch being recorded into a graph would replay the host epoch above: advance a device word first
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive) {
-        hipLaunchKernelGGL(epoch_bump_kernel, dim3(1), dim3(64), 0, stream, epoch_word);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        fa.epoch_word = epoch_word;
-    }
+    // advance the launch counter (eager or recorded alike), so that this launch's flag value is new
+    hipLaunchKernelGGL(fused_prepare_kernel, dim3(1), dim3(64), 0, stream, epoch_word, status);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     if (bmg == 16) launch_fused<16, false>(epi, grid, block, stream, fa);
     else if (bm == 128) launch_fused<128, false>(epi, grid, block, stream, fa);
     else launch_fused<128, true>(epi, grid, block, stream, fa);
@@ -1230,8 +1232,9 @@ hipError_t launch_expert_ffn(const GemmProblem& p, const uint8_t* x, const uint8
 }
 
 hipError_t launch_linear1(const GemmProblem& p, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
-                          const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf, hipStream_t stream) {
-    return launch_gemm<true>(p, linear1_args(p, x, x_sf, topk_w, w1, w1_sf, h_q, h_sf), stream);
+                          const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf, uint32_t* status,
+                          hipStream_t stream) {
+    return launch_gemm<true>(p, linear1_args(p, x, x_sf, topk_w, w1, w1_sf, h_q, h_sf, status), stream);
 }
 
 hipError_t launch_linear2(const GemmProblem& p, const uint8_t* h_q, const uint8_t* h_sf, const uint8_t* w2,

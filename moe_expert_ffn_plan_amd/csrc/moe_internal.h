@@ -96,7 +96,7 @@ inline ForwardLayout forward_layout(const moe_shape& s) {
     F.yslot = take((size_t)F.plan.cap * s.hidden * 2);
     F.flags = take((size_t)F.plan.max_tiles1 * 4);  // one word per Linear1 tile (fused launch)
     F.status = take(4);
-    F.epoch = take(4);  // advanced by single launches recorded into a graph
+    F.epoch = take(4);  // launch counter, advanced ahead of every single-launch GEMM
     F.total = o;
     return F;
 }
@@ -128,15 +128,17 @@ struct GemmProblem {
 // the top-k weights through the plan's row tables; Linear2 reads h_q and h_sf
 // (per-block layout [cap/bm][I/128][bm][4]) as the Linear1 epilogue wrote
 // them.  w*, w*_sf: weights in the tiled layout of moe_prepare.hip.
+// status: the forward's status word, cleared by the Linear1 launch (nothing in the two-launch schedule
+// sets it).
 hipError_t launch_linear1(const GemmProblem& g, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
-                          const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf,
+                          const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf, uint32_t* status,
                           hipStream_t stream);
 hipError_t launch_linear2(const GemmProblem& g, const uint8_t* h_q, const uint8_t* h_sf, const uint8_t* w2,
                           const uint8_t* w2_sf, uint16_t* yslot, hipStream_t stream);
 // Both GEMMs in one persistent launch when the shape allows it (fused_supported), else the two
-// launches above.  flags: one word per Linear1 tile, any initial contents; status: set to 1 if a
-// Linear2 tile stopped waiting for its rows (never cleared here); epoch_word: any initial contents,
-// advanced by a one-thread kernel ahead of the launch when the stream is being captured.
+// launches above.  flags: one word per Linear1 tile, any initial contents; status: cleared ahead of the
+// launch, set to 1 if a Linear2 tile stopped waiting for its rows; epoch_word: the workspace's launch
+// counter (any initial contents), advanced by a one-thread kernel ahead of every single launch.
 bool fused_supported(const moe_shape& s);
 // moe_forward runs both GEMMs as that one launch while Linear1 has at most kOneLaunchTilesPerCu tiles
 // per CU in the worst case (every hit local), else as two launches: the single launch hides the
@@ -151,7 +153,9 @@ hipError_t launch_expert_ffn(const GemmProblem& g, const uint8_t* x, const uint8
                              uint32_t* status, uint32_t* epoch_word, hipStream_t stream);
 hipError_t launch_tile_weights(int which, int N, int K, int E, const uint8_t* w, const uint8_t* w_sf,
                                uint8_t* w_out, uint8_t* sf_out, hipStream_t stream);
-hipError_t launch_combine(const moe_shape& s, const uint16_t* yslot, const int32_t* slot, uint16_t* y,
-                          hipStream_t stream);
+// status: the forward's status word; when it is non-zero (a single-launch GEMM gave up waiting) every
+// element of y is written as NaN.
+hipError_t launch_combine(const moe_shape& s, const uint16_t* yslot, const int32_t* slot, const uint32_t* status,
+                          uint16_t* y, hipStream_t stream);
 
 }  // namespace moe

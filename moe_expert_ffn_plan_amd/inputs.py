@@ -134,12 +134,13 @@ def _routing(w: Workload, g: torch.Generator, device, T: int):
 
 
 def make_inputs(w: Workload | str, device="cpu", num_tokens: int | None = None, seed: int | None = None,
-                weight_seed: int | None = None, with_weights: bool = True):
+                weight_seed: int | None = None, with_weights: bool = True, with_outlier_mask: bool = False):
     """Draw one workload.  Returns a dict of tensors on ``device``:
 
     x uint8 [T, H] (E4M3), x_sf uint8 [T, H/32], topk_idx int64 [T, k],
     topk_w float32 [T, k], w1 uint8 [E, 2I, H/2], w1_sf uint8 [E, 2I, H/32],
-    w2 uint8 [E, H, I/2], w2_sf uint8 [E, H, I/32].
+    w2 uint8 [E, H, I/2], w2_sf uint8 [E, H, I/32]; with ``with_outlier_mask``
+    also outlier bool [T], the tokens whose x was scaled before quantisation.
     Draw order: routing, top-k weights, x, outlier rows; then W1, W2 from
     their own generator.
     """
@@ -151,13 +152,17 @@ def make_inputs(w: Workload | str, device="cpu", num_tokens: int | None = None, 
     g.manual_seed(w.seed if seed is None else seed)
     ids, tw = _routing(w, g, device, T)
     x = torch.randn(T, H, generator=g, device=device)
+    outlier = torch.zeros(T, dtype=torch.bool, device=device)
     if w.outlier_frac > 0 and T > 0:
         perm = torch.randperm(T, generator=g, device=device)
         x[perm[: int(T * w.outlier_frac)]] *= w.outlier_scale
+        outlier[perm[: int(T * w.outlier_frac)]] = True
     xq, xsf = quantize_e4m3_blocks(x) if T > 0 else (torch.zeros(0, H, dtype=torch.uint8, device=device),
                                                    torch.zeros(0, H // 32, dtype=torch.uint8, device=device))
     out = {"x": xq.contiguous(), "x_sf": xsf.contiguous(), "topk_idx": ids.contiguous(),
            "topk_w": tw.contiguous()}
+    if with_outlier_mask:
+        out["outlier"] = outlier
     if with_weights:
         out.update(make_weights(w, device, weight_seed))
     return out

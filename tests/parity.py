@@ -12,13 +12,16 @@ Gates (one reading of the stated bars):
   BF16 input of the epilogue is not determined by the accumulation at all,
   since gfx950's scaled MFMA carries a dot-product error up to about
   2**-19 of the sum of |products| (measured), 32x below that threshold;
-* y (BF16): max |y - ref| <= 1e-2 * max |ref| + a, and
-  sum |y - ref| / sum |ref| <= 5e-3, where a (per element of y) is how far the
-  FP8 differences admitted above can move it: Linear2 is linear in h, so an
+* y (BF16): max |y - ref| <= 1e-2 * max |ref| and
+  sum |y - ref| / sum |ref| <= 5e-3, as stated, for every fixed case.
+  Only the seeded shape fuzz may widen the max clause, and only for a case
+  that fails it as stated: by a (per element of y), how far the FP8
+  differences admitted above can move it (Linear2 is linear in h, so an
   admitted difference of at most fp8_flip_bound in h[r, c] moves slot row r
-  by at most that times |W2[:, c]|, and the combine adds a token's slot rows.
-  Without such differences a = 0.  (One admitted flip of an element that
-  dominates its row moves that token's y by a few percent of max |ref|.)
+  by at most that times |W2[:, c]|, and the combine adds a token's slot
+  rows; one admitted flip of an element that dominates its row moves that
+  token's y by a few percent of max |ref|).  The fuzz reports how many
+  cases needed it.
 """
 import numpy as np
 
@@ -129,14 +132,22 @@ def fp8_flip_bound(q_ref, sf_ref):
     return 4.0 * np.ldexp(1.0, np.maximum(e - 1, -6) - 3) * s
 
 
-def assert_y_gate(y, ref, what="", allowance=None):
-    """The y gate above; `allowance` is a (per element of y, from the admitted FP8 differences)."""
+def y_gate_ok(y, ref, allowance=None):
+    """(passes, max clause value, mean clause value) of the y gate; `allowance` is the fuzz's a."""
     rel_max, rel_mean = y_errors(y, ref)
     if allowance is not None:
         m = float(np.abs(ref).max()) if ref.size else 0.0
         over = np.abs(np.asarray(y, np.float64) - ref) - allowance
         rel_max = float(max(over.max(), 0.0)) / m if m > 0 else float(max(over.max(), 0.0))
-    assert rel_max <= 1e-2 and rel_mean <= 5e-3, f"{what}: y max err {rel_max:.3e}, mean rel err {rel_mean:.3e}"
+    return rel_max <= 1e-2 and rel_mean <= 5e-3, rel_max, rel_mean
+
+
+def assert_y_gate(y, ref, what="", allowance=None):
+    """The y gate above (as stated when allowance is None)."""
+    ok, rel_max, rel_mean = y_gate_ok(y, ref, allowance)
+    assert np.all(np.isfinite(y)), f"{what}: y holds non-finite values"
+    assert ok, f"{what}: y max err {rel_max:.3e}, mean rel err {rel_mean:.3e}"
+    return rel_max, rel_mean
 
 
 def tile_columns(which):

@@ -119,3 +119,31 @@ def test_expert_ffn_full_size_matches_staged(gpu, name):
     for rep in range(2):
         _assert_same(_fused(s, d, plan_ws, ws), ref, f"{name} launch {rep}")
     assert int(status.item()) == 0
+
+
+@pytest.mark.parametrize("name", ["fused_bm32", "fallback"])
+def test_status_word_poisons_combine(gpu, name):
+    """A non-zero status word (what a single launch leaves when a Linear2 tile gave up waiting) makes
+    moe_combine write NaN over all of y; the next GEMM launch clears the word (the single launch's
+    prepare kernel, or moe_linear1 in the two-launch schedule) and y is whole again.  The word is set
+    from the host: no kernel is made to give up."""
+    w = CASES[name]
+    print(f"status word: {name} fused={runs_fused(w)}", flush=True)
+    s, d, plan_ws = _setup(w, gpu)
+    ws = torch.full((B.forward_workspace_bytes(s),), 0x5A, dtype=torch.uint8, device=gpu)
+    y = torch.empty(w.num_tokens, w.hidden, dtype=torch.bfloat16, device=gpu)
+    args = (d["x"], d["x_sf"], d["topk_idx"], d["topk_w"], d["w1"], d["w1_sf"], d["w2"], d["w2_sf"], y, ws)
+    B.forward(s, *args, plan_ws=plan_ws)
+    torch.cuda.synchronize()
+    good = y.clone()
+    status = B.forward_view(s, ws)["sync_status"]
+    assert int(status.item()) == 0
+    assert torch.isfinite(good.float()).all()
+    status.fill_(1)
+    B.combine(s, plan_ws, ws, y)
+    torch.cuda.synchronize()
+    assert torch.isnan(y.float()).all()
+    B.forward(s, *args, plan_ws=plan_ws)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    assert torch.equal(y.view(torch.int16), good.view(torch.int16))

@@ -1,8 +1,17 @@
 """GPU parity of the whole forward (moe_forward) against the CPU oracle.
 
-Small shapes are compared in full (FP8 intermediates of every valid row, y
-of every token); the full-size workloads compare sampled tokens, whose rows
-the oracle computes one by one, plus properties that hold at any size.
+Every fixed case is held to the gates as stated (routing tables bit-exact;
+FP8 intermediates within 1 ulp on at most 0.1% of the elements; y max |err|
+<= 1e-2 max |ref| and sum |err| / sum |ref| <= 5e-3):
+
+* the small shapes, tp_slice, decode and prefill are compared in full: the
+  FP8 intermediates of every valid row and y of every token;
+* skewed and dsv4 compare every token of a seeded sample of 2,048 (skewed,
+  at least 200 of them from the rows whose x was scaled by 50) or 1,024
+  (dsv4) tokens that covers every local expert: the FP8 intermediates of all
+  their rows and their y rows, which the oracle computes token by token,
+  plus properties that hold at any size (exact tables, y = +0 for tokens
+  without a local hit, no non-finite y).
 """
 import numpy as np
 import pytest
@@ -13,7 +22,7 @@ from moe_expert_ffn_plan_amd import inputs
 from oracle.forward import dequant_fp4_rows, dequant_fp8_rows, forward_ref, forward_tokens
 from oracle.routing import plan_ref
 from parity import (assert_fp8_gate, assert_plan_equal, assert_y_gate, bf16_to_f32, e4m3_step_distance,
-                    fp8_flip_bound, gpu_plan_to_numpy, linear1_cancellation, tile_columns)
+                    fp8_flip_bound, gpu_plan_to_numpy, linear1_cancellation, tile_columns, y_gate_ok)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,33 +43,52 @@ def run_gpu(w, d, dev, expert_begin=0, separate_plan=True, swiglu_limit=0.0, exa
     torch.cuda.synchronize()
     fv = B.forward_view(s, ws)
     pv = B.plan_view(s, plan_ws if plan_ws is not None else fv["plan_ws"])
+    assert int(fv["sync_status"].item()) == 0, "a Linear2 tile gave up waiting"
     return {"y": bf16_to_f32(y.cpu().numpy()), "h_q": fv["h_q"].cpu().numpy(), "h_sf": fv["h_sf"].cpu().numpy(),
             "plan": gpu_plan_to_numpy(pv, T, w.topk)}
 
 
-def check_full(w, d_cpu, out, expert_begin=0, swiglu_limit=0.0, fp8_rate=True):
-    d = inputs.to_numpy(d_cpu)
+def check_rows_fp8(d, q_g, s_g, q_r, s_r, tok, exp, what, rate=True):
+    """The FP8 gate over rows whose token and local expert are tok[i], exp[i].  The Linear1 cancellation
+    mask (exempting elements from the 1-ulp clause) is computed only for rows that hold a mismatch."""
+    bad = (e4m3_step_distance(q_g, q_r) > 0) | np.repeat(s_g != s_r, 32, axis=1)
+    cancel = np.zeros(bad.shape, bool)
+    rows = np.nonzero(bad.any(axis=1))[0]
+    for e in np.unique(exp[rows]):
+        rr = rows[exp[rows] == e]
+        t = tok[rr]
+        cancel[rr] = linear1_cancellation(dequant_fp8_rows(d["x"][t], d["x_sf"][t]),
+                                          dequant_fp4_rows(d["w1"][e], d["w1_sf"][e]))
+    return assert_fp8_gate(q_g, s_g, q_r, s_r, cancel, what, rate=rate)
+
+
+def check_full(w, d_cpu, out, expert_begin=0, swiglu_limit=0.0, fp8_rate=True, fuzz_allowance=False):
+    """Full comparison.  fuzz_allowance: the seeded shape fuzz may widen the y gate's max clause by the
+    carry of the admitted FP8 differences, only when the case fails it as stated (ref["y_widened"])."""
+    d = inputs.to_numpy(d_cpu) if isinstance(next(iter(d_cpu.values())), torch.Tensor) else d_cpu
     ref = forward_ref(d["x"], d["x_sf"], d["topk_idx"] - expert_begin, d["topk_w"], d["w1"], d["w1_sf"], d["w2"],
                       d["w2_sf"], num_experts=w.num_experts, expert_begin=0, block_m=w.block_m,
                       swiglu_limit=swiglu_limit)
     p = ref["plan"]
     assert_plan_equal(out["plan"], plan_ref(d["topk_idx"], w.num_experts, expert_begin, w.block_m))
-    valid = p.row_token >= 0
-    cancel = np.zeros((p.r_pad, w.intermediate), bool)
-    for e in range(w.num_experts):
-        rows = np.arange(p.offsets[e], p.offsets[e] + p.counts[e])
-        if rows.size:
-            tok = p.row_token[rows]
-            cancel[rows] = linear1_cancellation(dequant_fp8_rows(d["x"][tok], d["x_sf"][tok]),
-                                                dequant_fp4_rows(d["w1"][e], d["w1_sf"][e]))
-    ref["fp8_counts"] = assert_fp8_gate(out["h_q"][:p.r_pad][valid], out["h_sf"][:p.r_pad][valid],
-                                        ref["h_q"][valid], ref["h_sf"][valid], cancel[valid], w.name, rate=fp8_rate)
-    assert_y_gate(out["y"], ref["y"], w.name, allowance=fp8_flip_allowance(w, d, p, out, ref))
+    valid = np.nonzero(p.row_token >= 0)[0]
+    exp = np.searchsorted(p.offsets, valid, side="right") - 1
+    ref["fp8_counts"] = check_rows_fp8(d, out["h_q"][valid], out["h_sf"][valid], ref["h_q"][valid],
+                                       ref["h_sf"][valid], p.row_token[valid], exp, w.name, rate=fp8_rate)
+    ref["y_widened"] = False
+    if fuzz_allowance:
+        ok, _, _ = y_gate_ok(out["y"], ref["y"])
+        if not ok:
+            ref["y_widened"] = True
+            assert_y_gate(out["y"], ref["y"], w.name + " (FP8 carry allowance)",
+                          allowance=fp8_flip_allowance(w, d, p, out, ref))
+            return ref
+    ref["y_err"] = assert_y_gate(out["y"], ref["y"], w.name)
     return ref
 
 
 def fp8_flip_allowance(w, d, p, out, ref):
-    """How far the FP8 differences the gate admitted can move y (the y gate's term a): at every valid
+    """How far the FP8 differences the gate admitted can move y (the fuzz's term a): at every valid
     element whose (code, scale) differs from the oracle's, fp8_flip_bound of the oracle's value times
     |W2[:, c]| of the row's expert, added to the row's token."""
     r_pad = p.r_pad
@@ -138,12 +166,72 @@ def test_forward_internal_plan_and_expert_begin(gpu):
     check_full(w, d, out, expert_begin=40)
 
 
-def test_forward_tp_slice_full(gpu):
-    w = inputs.WORKLOADS["tp_slice"]
-    print("forward parity: tp_slice full size, whole output", flush=True)
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["tp_slice", "decode", "prefill"])
+def test_forward_full_size(gpu, name):
+    """The three smaller full-size workloads, every valid row and every token against the oracle."""
+    w = inputs.WORKLOADS[name]
+    print(f"forward parity: {name} full size, whole output", flush=True)
     d = inputs.make_inputs(w, device=gpu)
     out = run_gpu(w, d, gpu)
-    check_full(w, {k: v.cpu() for k, v in d.items()}, out)
+    ref = check_full(w, {k: v.cpu() for k, v in d.items()}, out)
+    print(f"{name}: FP8 mismatches {ref['fp8_counts'][0]} of {ref['fp8_counts'][1]}, y max err "
+          f"{ref['y_err'][0]:.3e} of max|ref|, mean rel err {ref['y_err'][1]:.3e}", flush=True)
+
+
+def _sample_tokens(w, ids, outlier, n, n_outliers, seed):
+    """A seeded sample of n tokens with a local hit: at least n_outliers outlier tokens, then others,
+    plus one token for each local expert the draw left out."""
+    local = (ids >= 0) & (ids < w.num_experts)
+    has = local.any(axis=1)
+    rng = np.random.default_rng(seed)
+    out_c = rng.permutation(np.nonzero(has & outlier)[0])[:n_outliers]
+    rest = rng.permutation(np.nonzero(has & ~outlier)[0])[:n - out_c.size]
+    chosen = set(out_c.tolist()) | set(rest.tolist())
+    covered = {int(e) for t in chosen for e in ids[t][local[t]]}
+    for e in range(w.num_experts):
+        if e not in covered:
+            t = int(np.nonzero((ids == e).any(axis=1))[0][0])
+            chosen.add(t)
+            covered |= {int(x) for x in ids[t][local[t]]}
+    return np.array(sorted(chosen))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,n,n_out", [("skewed", 2048, 200), ("dsv4", 1024, 0)])
+def test_forward_large_sampled(gpu, name, n, n_out):
+    w = inputs.WORKLOADS[name]
+    print(f"forward parity: {name} full size, {n} sampled tokens", flush=True)
+    d = inputs.make_inputs(w, device=gpu, with_outlier_mask=True)
+    outlier = d.pop("outlier").cpu().numpy()
+    out = run_gpu(w, d, gpu)
+    dn = inputs.to_numpy(d)
+    ids = dn["topk_idx"]
+    local = (ids >= 0) & (ids < w.num_experts)
+    # routing tables in full
+    p = plan_ref(ids, w.num_experts, 0, w.block_m)
+    assert_plan_equal(out["plan"], p)
+    # any size: tokens without a local hit give exactly +0; every y is finite
+    none = ~local.any(axis=1)
+    assert np.all(out["y"][none] == 0) and not np.any(np.signbit(out["y"][none]))
+    assert np.all(np.isfinite(out["y"]))
+    # the sample: every local expert, and (skewed) at least n_out of the x * 50 rows
+    chosen = _sample_tokens(w, ids, outlier, n, n_out, seed=7)
+    assert len({int(e) for t in chosen for e in ids[t][local[t]]}) == w.num_experts
+    assert int(outlier[chosen].sum()) >= n_out
+    yref, hits = forward_tokens(chosen, dn["x"], dn["x_sf"], ids, dn["topk_w"], dn["w1"], dn["w1_sf"], dn["w2"],
+                                dn["w2_sf"], num_experts=w.num_experts, expert_begin=0)
+    keys = list(hits)
+    q_g = np.stack([out["h_q"][p.slot[t, j]] for (t, j) in keys])
+    s_g = np.stack([out["h_sf"][p.slot[t, j]] for (t, j) in keys])
+    q_r = np.stack([hits[h][0] for h in keys])
+    s_r = np.stack([hits[h][1] for h in keys])
+    tok = np.array([t for (t, _) in keys])
+    exp = np.array([int(ids[t, j]) for (t, j) in keys])
+    bad, total = check_rows_fp8(dn, q_g, s_g, q_r, s_r, tok, exp, name)
+    err = assert_y_gate(out["y"][chosen], yref, name)
+    print(f"{name}: {chosen.size} tokens ({int(outlier[chosen].sum())} outliers), {len(keys)} rows; FP8 "
+          f"mismatches {bad} of {total}, y max err {err[0]:.3e} of max|ref|, mean rel err {err[1]:.3e}", flush=True)
 
 
 def _tile_reference(w, w_sf, N, K, which):
@@ -174,43 +262,3 @@ def test_prepare_weights_layout(gpu, which):
     want_w, want_sf = _tile_reference(d[key].numpy(), d[key + "_sf"].numpy(), N, K, which)
     assert np.array_equal(wt.cpu().numpy(), want_w)
     assert np.array_equal(sft.cpu().numpy(), want_sf)
-
-
-@pytest.mark.parametrize("name", ["decode", "prefill", "skewed", "dsv4"])
-def test_forward_large_sampled(gpu, name):
-    w = inputs.WORKLOADS[name]
-    print(f"forward parity: {name} full size, sampled tokens", flush=True)
-    d = inputs.make_inputs(w, device=gpu)
-    out = run_gpu(w, d, gpu)
-    dn = inputs.to_numpy(d)
-    ids = dn["topk_idx"]
-    local = (ids >= 0) & (ids < w.num_experts)
-    # routing tables in full
-    p = plan_ref(ids, w.num_experts, 0, w.block_m)
-    assert_plan_equal(out["plan"], p)
-    # tokens without a local hit give exactly +0
-    none = ~local.any(axis=1)
-    assert np.all(out["y"][none] == 0) and not np.any(np.signbit(out["y"][none]))
-    # sampled tokens: a few with hits on a small set of experts (bounds the oracle's work)
-    rng = np.random.default_rng(7)
-    cand = np.nonzero(local.any(axis=1))[0]
-    chosen, experts = [], set()
-    for t in rng.permutation(cand):
-        es = set(ids[t][local[t]].tolist())
-        if len(experts | es) <= 6:
-            chosen.append(int(t))
-            experts |= es
-        if len(chosen) >= 12:
-            break
-    chosen = np.array(sorted(chosen))
-    yref, hits = forward_tokens(chosen, dn["x"], dn["x_sf"], ids, dn["topk_w"], dn["w1"], dn["w1_sf"], dn["w2"],
-                                dn["w2_sf"], num_experts=w.num_experts, expert_begin=0)
-    q_g = np.stack([out["h_q"][p.slot[t, j]] for (t, j) in hits])
-    s_g = np.stack([out["h_sf"][p.slot[t, j]] for (t, j) in hits])
-    q_r = np.stack([v[0] for v in hits.values()])
-    s_r = np.stack([v[1] for v in hits.values()])
-    w1_deq = {e: dequant_fp4_rows(dn["w1"][e], dn["w1_sf"][e]) for e in experts}
-    cancel = np.concatenate([linear1_cancellation(dequant_fp8_rows(dn["x"][[t]], dn["x_sf"][[t]]),
-                                                  w1_deq[int(ids[t, j])]) for (t, j) in hits])
-    assert_fp8_gate(q_g, s_g, q_r, s_r, cancel, name)
-    assert_y_gate(out["y"][chosen], yref, name)

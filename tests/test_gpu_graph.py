@@ -84,3 +84,69 @@ def test_forward_graph_replays(gpu, name):
         want = _eager(s, new, gpu)  # eager work between replays
         assert torch.equal(y.view(torch.int16), want.view(torch.int16)), f"{name}: replay {rep} differs from eager"
     assert int(status.item()) == 0, "a Linear2 tile gave up waiting"
+
+
+@pytest.mark.parametrize("fill", [0x00, 0x5A, 0xFF])
+def test_graphs_share_workspace(gpu, fill):
+    """Two forwards (two layers: different weights) recorded into one graph on ONE workspace, a second
+    graph with the layers in the other order on the same workspace, and eager calls on it in between.
+    Every launch on the workspace must stamp completion flags no earlier launch stamped, whatever the
+    workspace held at first; each output is compared bit for bit with an eager run on a fresh
+    workspace."""
+    w = CASES["one_launch"]
+    s = B.shape_of(w)
+    assert B.forward_uses_expert_ffn(s)
+    print(f"graph replay: two layers on one workspace, fill 0x{fill:02X}", flush=True)
+    layers = []
+    for ws_seed in (71, 171):
+        lw = {k: v.to(gpu) for k, v in inputs.make_weights(w, device="cpu", weight_seed=ws_seed).items()}
+        lw.update(B.prepare_all(s, lw))
+        layers.append(lw)
+    static = {k: v.to(gpu) for k, v in inputs.make_inputs(w, device="cpu", seed=200, with_weights=False).items()}
+    ws = torch.full((B.forward_workspace_bytes(s),), fill, dtype=torch.uint8, device=gpu)
+    plan_ws = torch.empty(B.plan_workspace_bytes(s), dtype=torch.uint8, device=gpu)
+    ys = [torch.empty(w.num_tokens, w.hidden, dtype=torch.bfloat16, device=gpu) for _ in range(2)]
+
+    def run(order):
+        B.plan(s, static["topk_idx"], plan_ws)
+        for li, yi in zip(order, (0, 1)):
+            lw = layers[li]
+            B.forward(s, static["x"], static["x_sf"], static["topk_idx"], static["topk_w"], lw["w1"], lw["w1_sf"],
+                      lw["w2"], lw["w2_sf"], ys[yi], ws, plan_ws=plan_ws)
+
+    def expect(order):
+        d = dict(static)
+        return [_eager(s, {**d, **layers[li]}, gpu) for li in order]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run((0, 1))  # eager call before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = {}
+    for order in ((0, 1), (1, 0)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(order)
+        graphs[order] = g
+    torch.cuda.synchronize()
+    status = B.forward_view(s, ws)["sync_status"]
+    seq = [("g", (0, 1)), ("g", (1, 0)), ("e", (0, 1)), ("g", (0, 1)), ("g", (0, 1)), ("e", (1, 0)),
+           ("g", (1, 0)), ("g", (0, 1))]
+    for rep, (kind, order) in enumerate(seq):
+        new = {k: v.to(gpu) for k, v in inputs.make_inputs(w, device="cpu", seed=300 + rep,
+                                                           with_weights=False).items()}
+        for key in ("x", "x_sf", "topk_idx", "topk_w"):
+            static[key].copy_(new[key])
+        torch.cuda.synchronize()
+        if kind == "g":
+            graphs[order].replay()
+        else:
+            run(order)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, f"step {rep}: a Linear2 tile gave up waiting"
+        got = [y.view(torch.int16).clone() for y in ys]
+        want = expect(order)
+        for li in range(2):
+            assert torch.equal(got[li], want[li].view(torch.int16)), f"step {rep} ({kind}{order}) layer {li} differs"

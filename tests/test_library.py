@@ -151,3 +151,26 @@ def test_gemm_launches_named_workloads():
     got = {n: B.gemm_launches(B.shape_of(w)) for n, w in inputs.WORKLOADS.items()}
     assert got["tiny"] == (2, 2) and got["decode"] == (1, 1) and got["prefill"] == (1, 1)
     assert got["tp_slice"] == (1, 1) and got["skewed"] == (1, 2) and got["dsv4"] == (1, 2)
+
+
+def test_plain_weight_layout_refused():
+    """The calls that read weights take only the tiled layout and say so before looking at any pointer;
+    the others ignore the field, and an undefined layout value is a shape error."""
+    lib = B.lib()
+    plain = B.make_shape(64, 256, 128, 8, 2, 128, weight_layout=B.WEIGHTS_PLAIN)
+    assert B.WEIGHTS_PLAIN == 0 and B.MoeShape().weight_layout == B.WEIGHTS_PLAIN  # a zeroed shape is plain
+    sp = ctypes.byref(plain)
+    assert lib.moe_forward(sp, *([None] * 11), 0, None) == -7
+    assert lib.moe_linear1(sp, *([None] * 7), 0, None) == -7
+    assert lib.moe_linear2(sp, *([None] * 4), 0, None) == -7
+    assert lib.moe_expert_ffn(sp, *([None] * 9), 0, None) == -7
+    assert B.status_str(-7) == "weights not declared in the tiled layout"
+    empty = B.make_shape(0, 256, 128, 8, 2, 128, weight_layout=B.WEIGHTS_PLAIN)
+    assert lib.moe_forward(ctypes.byref(empty), *([None] * 11), 0, None) == -7
+    v = ctypes.c_size_t()
+    assert lib.moe_forward_workspace_bytes(sp, ctypes.byref(v)) == 0
+    assert lib.moe_plan(sp, None, None, 0, None) == -1          # routing reads no weights
+    tiled = B.make_shape(64, 256, 128, 8, 2, 128)
+    assert lib.moe_forward(ctypes.byref(tiled), *([None] * 11), 0, None) == -1
+    odd = B.make_shape(64, 256, 128, 8, 2, 128, weight_layout=2)
+    assert lib.moe_forward_workspace_bytes(ctypes.byref(odd), ctypes.byref(v)) == -2
