@@ -109,6 +109,27 @@ def linear1_cancellation(a_rows, w1_rows_deq):
     return (np.abs(zg) < 2.0 ** -14 * sg) | (np.abs(zu) < 2.0 ** -14 * su)
 
 
+def linear1_cancellation_at(a_rows, w1_rows_of, chans):
+    """For elements i (activation row a_rows[i] of one expert, SwiGLU channel chans[i]): whether the exact
+    gate or up sum is within 2**-14 * sum|products| of zero.  w1_rows_of(rows) returns the expert's
+    dequantized W1 rows (interleaved order); the channel -> row map is the oracle's de-interleave."""
+    from oracle.forward import deinterleave_gate_up
+    out = np.zeros(len(chans), bool)
+    if len(chans) == 0:
+        return out
+    n2 = 2 * (int(chans.max()) // 8 + 1) * 8
+    gate_row, up_row = deinterleave_gate_up(np.arange(n2))
+    for i0 in range(0, len(chans), 4096):
+        a = a_rows[i0:i0 + 4096]
+        ch = chans[i0:i0 + 4096]
+        for rows in (gate_row[ch], up_row[ch]):
+            w = w1_rows_of(rows)
+            z = np.einsum("ij,ij->i", a, w)
+            s = np.einsum("ij,ij->i", np.abs(a), np.abs(w))
+            out[i0:i0 + 4096] |= np.abs(z) < 2.0 ** -14 * s
+    return out
+
+
 def bf16_to_f32(bits_i16: np.ndarray) -> np.ndarray:
     return (bits_i16.astype(np.uint16).astype(np.uint32) << 16).view(np.float32)
 

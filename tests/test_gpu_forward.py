@@ -4,14 +4,14 @@ Every fixed case is held to the gates as stated (routing tables bit-exact;
 FP8 intermediates within 1 ulp on at most 0.1% of the elements; y max |err|
 <= 1e-2 max |ref| and sum |err| / sum |ref| <= 5e-3):
 
-* the small shapes, tp_slice, decode and prefill are compared in full: the
-  FP8 intermediates of every valid row and y of every token;
-* skewed and dsv4 compare every token of a seeded sample of 2,048 (skewed,
-  at least 200 of them from the rows whose x was scaled by 50) or 1,024
-  (dsv4) tokens that covers every local expert: the FP8 intermediates of all
-  their rows and their y rows, which the oracle computes token by token,
-  plus properties that hold at any size (exact tables, y = +0 for tokens
-  without a local hit, no non-finite y).
+* the small shapes, tp_slice, decode, prefill and skewed are compared in
+  full: the FP8 intermediates of every valid row and y of every token;
+* dsv4 (about 52 TFLOP for the oracle in full) compares every token of a
+  seeded sample of 1,024 tokens that covers every local expert: the FP8
+  intermediates of all their rows and their y rows, which the oracle
+  computes token by token, plus properties that hold at any size (exact
+  tables, y = +0 for tokens without a local hit, no non-finite y).  The y
+  gate's max clause is then taken over the sample (its own max |ref|).
 """
 import numpy as np
 import pytest
@@ -22,7 +22,7 @@ from moe_expert_ffn_plan_amd import inputs
 from oracle.forward import dequant_fp4_rows, dequant_fp8_rows, forward_ref, forward_tokens
 from oracle.routing import plan_ref
 from parity import (assert_fp8_gate, assert_plan_equal, assert_y_gate, bf16_to_f32, e4m3_step_distance,
-                    fp8_flip_bound, gpu_plan_to_numpy, linear1_cancellation, tile_columns, y_gate_ok)
+                    fp8_flip_bound, gpu_plan_to_numpy, linear1_cancellation_at, tile_columns, y_gate_ok)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,15 +50,17 @@ def run_gpu(w, d, dev, expert_begin=0, separate_plan=True, swiglu_limit=0.0, exa
 
 def check_rows_fp8(d, q_g, s_g, q_r, s_r, tok, exp, what, rate=True):
     """The FP8 gate over rows whose token and local expert are tok[i], exp[i].  The Linear1 cancellation
-    mask (exempting elements from the 1-ulp clause) is computed only for rows that hold a mismatch."""
+    mask (exempting elements from the 1-ulp clause) is computed only at the elements that differ."""
     bad = (e4m3_step_distance(q_g, q_r) > 0) | np.repeat(s_g != s_r, 32, axis=1)
     cancel = np.zeros(bad.shape, bool)
-    rows = np.nonzero(bad.any(axis=1))[0]
+    rows, chans = np.nonzero(bad)
     for e in np.unique(exp[rows]):
-        rr = rows[exp[rows] == e]
-        t = tok[rr]
-        cancel[rr] = linear1_cancellation(dequant_fp8_rows(d["x"][t], d["x_sf"][t]),
-                                          dequant_fp4_rows(d["w1"][e], d["w1_sf"][e]))
+        sel = exp[rows] == e
+        r, c = rows[sel], chans[sel]
+        t = tok[r]
+        a = dequant_fp8_rows(d["x"][t], d["x_sf"][t])
+        cancel[r, c] = linear1_cancellation_at(
+            a, lambda wr: dequant_fp4_rows(d["w1"][e][wr], d["w1_sf"][e][wr]), c)
     return assert_fp8_gate(q_g, s_g, q_r, s_r, cancel, what, rate=rate)
 
 
@@ -167,9 +169,9 @@ def test_forward_internal_plan_and_expert_begin(gpu):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["tp_slice", "decode", "prefill"])
+@pytest.mark.parametrize("name", ["tp_slice", "decode", "prefill", "skewed"])
 def test_forward_full_size(gpu, name):
-    """The three smaller full-size workloads, every valid row and every token against the oracle."""
+    """Four full-size workloads, every valid row and every token against the oracle."""
     w = inputs.WORKLOADS[name]
     print(f"forward parity: {name} full size, whole output", flush=True)
     d = inputs.make_inputs(w, device=gpu)
@@ -198,7 +200,7 @@ def _sample_tokens(w, ids, outlier, n, n_outliers, seed):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,n,n_out", [("skewed", 2048, 200), ("dsv4", 1024, 0)])
+@pytest.mark.parametrize("name,n,n_out", [("dsv4", 1024, 0)])
 def test_forward_large_sampled(gpu, name, n, n_out):
     w = inputs.WORKLOADS[name]
     print(f"forward parity: {name} full size, {n} sampled tokens", flush=True)

@@ -97,3 +97,19 @@ def test_y_gate_allowance_admits_only_the_propagated_amount():
         except AssertionError:
             ok = False
         assert ok == passes
+
+
+def test_cancellation_at_matches_rowwise():
+    """The element-wise Linear1 cancellation mask agrees with the row-wise one at every element."""
+    from parity import linear1_cancellation, linear1_cancellation_at
+    rng = np.random.default_rng(5)
+    H, I = 256, 64
+    a = rng.standard_normal((6, H))
+    w1 = rng.standard_normal((2 * I, H))
+    # make some exact sums cancel: copy a row of W1 with a sign flip half way
+    w1[3, H // 2:] = -w1[3, :H // 2] * (a[2, :H // 2] / a[2, H // 2:])
+    full = linear1_cancellation(a, w1)
+    assert full.any() and not full.all()
+    r, c = np.nonzero(np.ones_like(full))
+    got = linear1_cancellation_at(a[r], lambda rows: w1[rows], c)
+    assert np.array_equal(got, full[r, c])
