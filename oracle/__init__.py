@@ -18,7 +18,9 @@ the pages' description step by step:
 Parity pins: every function is pinned by tests under ``tests/`` marked
 ``not gpu`` (exhaustive codec tables, library casts, brute force, exact
 rational arithmetic, closed-form invariants).  The SiLU step has no printed
-value on the pages and is pinned only by its closed form (see
-``forward.swiglu_weight``).
+value on the pages; it is pinned by an independent per-token reference built
+from library routines (torch's float8/bfloat16 casts and
+``torch.nn.functional.silu`` in float64), which the whole forward matches bit
+for bit.  No function is left unpinned.
 """
 from . import formats, routing, forward  # noqa: F401

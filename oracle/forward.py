@@ -74,8 +74,9 @@ def swiglu_weight(z_gate: np.ndarray, z_up: np.ndarray, w: np.ndarray, limit: fl
     """h = fl32(fl32(silu(bf16(g)) * bf16(u)) * w); w broadcasts per row.  With limit > 0,
     g = min(bf16(g), limit) and u = clip(bf16(u), -limit, limit) first.
 
-    Parity unpinned beyond this closed form: the pages print no numeric
-    example of the epilogue.
+    The pages print no numeric example of the epilogue; the step is pinned
+    by an independent per-token reference that evaluates it with torch's
+    silu and casts (the forward matches it bit for bit).
     """
     g = F.bf16_rne(z_gate)
     u = F.bf16_rne(z_up)
