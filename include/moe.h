@@ -334,6 +334,38 @@ typedef struct moe_forward_view {
 } moe_forward_view;
 MOE_API int moe_forward_view_get(const moe_shape* shape, void* ws, moe_forward_view* out);
 
+/* ---- forward without a caller workspace -----------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture that must not call hipMalloc, tight serving loops, harnesses that
+ * forbid allocation.  moe_forward_noalloc computes exactly what moe_forward
+ * computes with plan_ws = NULL (the same kernels, bit for bit), but its
+ * forward workspace (routing tables included) is a device array inside the
+ * library of MOE_NOALLOC_WORKSPACE_BYTES bytes per GPU, which every GPU the
+ * library runs it on holds until the process ends.  The caller passes only
+ * inputs and outputs, with moe_forward's meaning, layout and alignment.
+ *   - Shapes whose moe_forward_workspace_bytes exceeds
+ *     MOE_NOALLOC_WORKSPACE_BYTES are refused with MOE_ERR_WORKSPACE before
+ *     any GPU work (the decode-sized batches fit: 128 tokens, hidden 7168,
+ *     intermediate 2048, 32 experts, top-8, block_m 16 needs ~25 MB).
+ *   - No call allocates or frees device memory, and none enqueues a memset.
+ *     The first call on a device resolves the array's address there (call
+ *     once eagerly before capturing a graph).
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents; nothing in it must start at zero (tables are rebuilt,
+ *     completion flags are stamped from a launch counter, the status word is
+ *     cleared by every GEMM launch).  Calls that overlap in time on one GPU
+ *     (different streams, or different host threads) race on the array and
+ *     give undefined results: serialise them.
+ * Validation as for moe_forward; MOE_ERR_HIP also if the array's address
+ * cannot be resolved. */
+#define MOE_NOALLOC_WORKSPACE_BYTES (32u << 20)
+MOE_API int moe_forward_noalloc(const moe_shape* shape,
+                const uint8_t* x, const uint8_t* x_sf,
+                const int64_t* topk_idx, const float* topk_w,
+                const uint8_t* w1, const uint8_t* w1_sf,
+                const uint8_t* w2, const uint8_t* w2_sf,
+                uint16_t* y, void* stream);
+
 /* MOE_OK if `device` is a gfx950 GPU, MOE_ERR_ARCH if not, MOE_ERR_HIP if
  * the runtime cannot be queried. */
 MOE_API int moe_device_supported(int device);

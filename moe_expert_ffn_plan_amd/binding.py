@@ -49,7 +49,7 @@ _lib = None
 
 EXPORTS = ["moe_capacity_rows", "moe_suggest_block_m", "moe_gemm_launches", "moe_plan_workspace_bytes", "moe_plan", "moe_plan_view_get",
            "moe_forward_workspace_bytes", "moe_forward", "moe_linear1", "moe_linear2", "moe_combine",
-           "moe_expert_ffn", "moe_prepare_weights",
+           "moe_expert_ffn", "moe_prepare_weights", "moe_forward_noalloc",
            "moe_forward_view_get", "moe_device_supported", "moe_status_str"]
 
 
@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
         L.moe_plan.argtypes = [S, VP, VP, SZ, VP]
         L.moe_plan_view_get.argtypes = [S, VP, P(PlanView)]
         L.moe_forward.argtypes = [S, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
+        L.moe_forward_noalloc.argtypes = [S, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP]
         L.moe_prepare_weights.argtypes = [S, ctypes.c_int, VP, VP, VP, VP, VP]
         L.moe_linear1.argtypes = [S, VP, VP, VP, VP, VP, VP, VP, SZ, VP]
         L.moe_linear2.argtypes = [S, VP, VP, VP, VP, SZ, VP]
@@ -196,6 +197,27 @@ def forward(shape: MoeShape, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y,
     args.append(_ptr(plan_ws, u8, "plan_ws", dev))
     st = lib().moe_forward(ctypes.byref(shape), *args, _ptr(ws, u8, "ws"), ws.numel(), _stream(stream))
     _check("moe_forward", st)
+
+
+NOALLOC_WORKSPACE_BYTES = 32 << 20   # MOE_NOALLOC_WORKSPACE_BYTES
+
+
+def forward_noalloc(shape: MoeShape, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y, stream=None) -> None:
+    """moe_forward_noalloc: moe_forward (routing included) with the library's own device workspace."""
+    T, H, I, E, k = shape.num_tokens, shape.hidden, shape.intermediate, shape.num_experts, shape.topk
+    dev = y.device
+    u8, args = torch.uint8, []
+    args.append(_ptr(x, u8, "x", dev, T * H))
+    args.append(_ptr(x_sf, u8, "x_sf", dev, T * H // 32))
+    args.append(_ptr(topk_idx, torch.int64, "topk_idx", dev, T * k))
+    args.append(_ptr(topk_w, torch.float32, "topk_w", dev, T * k))
+    args.append(_ptr(w1, u8, "w1", dev, E * 2 * I * H // 2))
+    args.append(_ptr(w1_sf, u8, "w1_sf", dev, E * 2 * I * H // 32))
+    args.append(_ptr(w2, u8, "w2", dev, E * H * I // 2))
+    args.append(_ptr(w2_sf, u8, "w2_sf", dev, E * H * I // 32))
+    yv = y.view(torch.int16) if y.dtype == torch.bfloat16 else y
+    args.append(_ptr(yv, torch.int16, "y", dev, T * H))
+    _check("moe_forward_noalloc", lib().moe_forward_noalloc(ctypes.byref(shape), *args, _stream(stream)))
 
 
 def prepare_weights(shape: MoeShape, which: int, w, w_sf, stream=None):

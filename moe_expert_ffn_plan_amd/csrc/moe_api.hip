@@ -7,6 +7,7 @@
 // answer "unsupported" (reading notes, "host-side checks").
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -306,6 +307,60 @@ int moe_forward(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, c
         if ((st = moe_linear2(shape, w2, w2_sf, plan, ws, ws_bytes, stream)) != MOE_OK) return st;
     }
     return moe_combine(shape, plan, ws, ws_bytes, y, stream);
+}
+
+// ---- allocation-free forward (moe_forward_noalloc)
+// Its workspace is this file-scope device array: one copy per GPU, held until the process ends.  In
+// host code the name `scratch` is only a host-side stand-in; the array's device address on a GPU comes
+// from hipGetSymbolAddress, called once per device with that device current, and only that address is
+// ever passed to kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_WORKSPACE_BYTES];
+
+}  // extern "C"
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (resolved on the first call on that device).
+int scratch_of_current_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_noalloc(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, const int64_t* topk_idx,
+                        const float* topk_w, const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2,
+                        const uint8_t* w2_sf, uint16_t* y, void* stream) {
+    int st = check_weight_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->num_tokens == 0) return MOE_OK;
+    if (!x || !x_sf || !topk_idx || !topk_w || !w1 || !w1_sf || !w2 || !w2_sf || !y) return MOE_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(x_sf, 16) || !aligned(w1, 16) || !aligned(w1_sf, 16) || !aligned(w2, 16) ||
+        !aligned(w2_sf, 16) || !aligned(y, 16) || !aligned(topk_idx, 8) || !aligned(topk_w, 4))
+        return MOE_ERR_ALIGN;
+    if (forward_layout(*shape).total > (size_t)MOE_NOALLOC_WORKSPACE_BYTES) return MOE_ERR_WORKSPACE;
+    if ((st = check_arch_current()) != MOE_OK) return st;
+    void* ws = nullptr;
+    if ((st = scratch_of_current_device(&ws)) != MOE_OK) return st;
+    // the routing tables go to the plan region of the workspace (plan_ws = NULL)
+    return moe_forward(shape, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y, nullptr, ws,
+                       (size_t)MOE_NOALLOC_WORKSPACE_BYTES, stream);
 }
 
 }  // extern "C"

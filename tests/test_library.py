@@ -174,3 +174,18 @@ def test_plain_weight_layout_refused():
     assert lib.moe_forward(ctypes.byref(tiled), *([None] * 11), 0, None) == -1
     odd = B.make_shape(64, 256, 128, 8, 2, 128, weight_layout=2)
     assert lib.moe_forward_workspace_bytes(ctypes.byref(odd), ctypes.byref(v)) == -2
+
+
+def test_noalloc_size_limit():
+    """moe_forward_noalloc refuses shapes whose workspace exceeds its array, before any GPU work; the
+    decode-sized batch fits."""
+    from moe_expert_ffn_plan_amd import inputs
+    lib = B.lib()
+    big = B.shape_of(inputs.WORKLOADS["tp_slice"])
+    assert B.forward_workspace_bytes(big) > B.NOALLOC_WORKSPACE_BYTES
+    fake = [ctypes.c_void_p(0x10000)] * 9
+    assert lib.moe_forward_noalloc(ctypes.byref(big), *fake, None) == -4
+    assert B.forward_workspace_bytes(B.shape_of(inputs.WORKLOADS["decode"])) <= B.NOALLOC_WORKSPACE_BYTES
+    plain = B.make_shape(64, 256, 128, 8, 2, 128, weight_layout=B.WEIGHTS_PLAIN)
+    assert lib.moe_forward_noalloc(ctypes.byref(plain), *fake, None) == -7
+    assert lib.moe_forward_noalloc(ctypes.byref(B.make_shape(64, 256, 128, 8, 2, 128)), *([None] * 9), None) == -1
