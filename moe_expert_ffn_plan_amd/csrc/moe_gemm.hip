@@ -690,13 +690,17 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
 // its stores at device scope), one lane stores the launch's epoch into that
 // tile's flag.  In the Linear2 run group 1 also loads the flags of tile
 // ci + 1's M-tile with its row tables (gate[.. % 3], read device-coherent),
-// and before it issues a tile's first stage it checks that all of them hold
-// the epoch, else sleeps and loads them again.  A workgroup's own Linear1
-// tiles are all flagged before its Linear2 run starts, every workgroup runs
-// its Linear1 tiles first, and the grid is at most one workgroup per CU, all
-// resident: every awaited tile is being computed.  A Linear2 tile reads only
-// rows whose Linear1 tiles are done and no XCD reads those lines earlier in
-// the launch, so plain loads see the stored values.  After kGateSpins polls
+// and before it issues the activation DMA of K-step kt it checks that the
+// flag of Linear1 N-tile kt / 2, the one that wrote those 128 channels,
+// holds the epoch, else sleeps and loads the flags again.  A workgroup's own
+// Linear1 tiles are all flagged before its Linear2 run starts, every
+// workgroup runs its Linear1 tiles first, and the grid is at most one
+// workgroup per CU, all resident: every awaited tile is being computed.  A
+// Linear2 K-step reads only channels whose Linear1 tile is done, and no XCD
+// reads those lines earlier in the launch (a row's 128 channels of one
+// K-step are one 128-byte line of h_q; its scale words of K-steps 2m and
+// 2m + 1, which can share a line when block_m is 16, come from the same
+// Linear1 tile), so plain loads see the stored values.  After kGateSpins polls
 // the wait gives up and sets the status word instead of hanging (the tile
 // then computes on rows that may be unfinished, and the combine, which reads
 // the word, writes NaN over all of y).
@@ -874,16 +878,31 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
         if constexpr (FUSED) __syncthreads();  // B_S
     } else {
         StageDma<BM, 512, C::A_PW, 1, BM == 16 || PARTIAL> dma;
-        // fused Linear2: wait until every Linear1 tile of t's M-tile is done.  The flags came with
-        // the row tables; while one is not set yet, sleep and load them again (the wait for that load
-        // drains this wave's DMA queue, which only makes the later vmcnt waits conservative)
-        auto gate_open = [&](int j, const TileId& t) {
+        // fused Linear2: before the activation DMA of K-step kt of tile j, wait until the Linear1 tile
+        // that wrote those channels of t's rows is done.  Linear2 K-step kt reads h channels
+        // [128 kt, 128 kt + 128), which Linear1 N-tile kt / 2 (256 SwiGLU channels, 512 gate/up
+        // columns) produced, so a K-step needs one flag, not the whole M-tile's (the reading notes'
+        // per-K-block gating).  The flags of the M-tile came with the row tables.  At a tile's first
+        // stage all of them are looked at once; when they are all set (the usual case: an M-tile's
+        // Linear1 tiles run side by side and finish together) the tile's later stages check nothing.
+        // Otherwise each K-step waits for its own flag: while it is not set, sleep and load the flags
+        // again (the wait for that load drains this wave's DMA queue, which only makes the later
+        // vmcnt waits conservative), and stop checking once all are set.
+        bool gate_all = false;  // every flag of the issuing tile's M-tile holds the epoch
+        auto gate_open = [&](int j, const TileId& t, int kt) {
             if constexpr (C::GATED) {
                 const uint32_t* fl = sh.gate[j % kTableSlots];
+                if (kt == 0) gate_all = false;
+                if (gate_all) return;
+                const int need = kt >> 1;
                 for (int it = 0;; ++it) {
                     const int l = fresh_lane();
                     const bool ok = l >= sync.nt1 || fl[l] == sync.epoch;
-                    if (__builtin_amdgcn_ballot_w64(!ok) == 0) return;
+                    if (__builtin_amdgcn_ballot_w64(!ok) == 0) {
+                        gate_all = true;
+                        return;
+                    }
+                    if (__builtin_amdgcn_readfirstlane(fl[need]) == sync.epoch) return;
                     if (it == kGateSpins) {
                         if (l == 0) __hip_atomic_store(sync.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         return;
@@ -894,7 +913,7 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
                 }
             }
         };
-        gate_open(0, t0);
+        TileId itile = t0;  // tile whose stages are being issued
         dma.init_a(g, t0.m, t0.rows, sh.meta[0], L1, wq, 4);
         dma.init_b(g, t0, wq, 4);
         TileId tn;  // tile whose rows the table load fetches
@@ -909,13 +928,12 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
         uint32_t w_off = L1 ? weight_offset(0, t0.rows) : 0u;
         auto issue = [&](int s) {
             if (s % KT == 0 && s > 0) {
-                TileId t;
-                read_entry(s / KT, t);
-                gate_open(s / KT, t);
-                dma.init_a(g, t.m, t.rows, sh.meta[(s / KT) % kTableSlots], L1, wq, 4);
-                dma.init_b(g, t, wq, 4);
-                if (L1) w_off = weight_offset(s / KT, t.rows);
+                read_entry(s / KT, itile);
+                dma.init_a(g, itile.m, itile.rows, sh.meta[(s / KT) % kTableSlots], L1, wq, 4);
+                dma.init_b(g, itile, wq, 4);
+                if (L1) w_off = weight_offset(s / KT, itile.rows);
             }
+            gate_open(s / KT, itile, s % KT);
             dma.issue_a(sh.smem + (s % L::NS) * L::STAGE, s % KT, lane);
             dma.template issue_b_blocks<C::B1_PW, 4 * C::B0_PW>(sh.smem + (s % L::NS) * L::STAGE, s % KT, lane);
             load_meta(max(s - (L::NS - 1), 0) / KT + 1, tn);
