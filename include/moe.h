@@ -78,7 +78,8 @@ enum moe_weight_layout {
  *   num_experts  E local experts, 1..512
  *   expert_begin global id of local expert 0
  *   topk         k, 1..64
- *   block_m      rows per routing block, one of 16, 32, 64, 128; each
+ *   block_m      rows per routing block, one of 16, 32, 64, 96, 128, 192
+ *                (the walk-through's BLOCK_M candidates, section 7.1); each
  *                expert's rows are padded to a multiple of it.
  * Linear1 epilogue variants (reading notes, "activation clamp" and the
  * fast-math switch of the SwiGLU step; walk-through section 4.6):
@@ -123,7 +124,8 @@ MOE_API int moe_capacity_rows(const moe_shape* shape, int64_t* rows);
 /* Routing block heuristic (walk-through section 7.1, "BLOCK_M selection"):
  * the expected rows per expert, num_tokens * topk / num_experts, times the
  * pages' imbalance factor 2 is the target; the result is the smallest
- * supported block_m (16, 32, 64, 128) that is >= the target, else 128.
+ * candidate of the pages' ladder (16, 32, 64, 96, 128, 192) that is >= the
+ * target, else 192.
  *   num_tokens   tokens whose top-k lists are routed (all ranks' tokens,
  *                num_tokens x num_ranks in the pages' formula), >= 0
  *   topk         k, 1..64

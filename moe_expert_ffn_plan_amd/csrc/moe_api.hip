@@ -30,7 +30,7 @@ int check_shape(const moe_shape* s) {
     if (s->num_tokens < 0 || s->hidden <= 0 || s->intermediate <= 0) return MOE_ERR_SHAPE;
     if (s->num_experts < 1 || s->num_experts > kMaxExperts) return MOE_ERR_SHAPE;
     if (s->topk < 1 || s->topk > kMaxTopk) return MOE_ERR_SHAPE;
-    if (!(s->block_m == 16 || s->block_m == 32 || s->block_m == 64 || s->block_m == 128)) return MOE_ERR_SHAPE;
+    if (!block_m_supported(s->block_m)) return MOE_ERR_SHAPE;
     if ((int64_t)s->num_tokens * s->topk >= (1ll << 30)) return MOE_ERR_SHAPE;
     if (!(s->swiglu_limit >= 0.0f && s->swiglu_limit <= 3.0e38f)) return MOE_ERR_SHAPE;  // also rejects NaN
     if (s->exact_silu != 0 && s->exact_silu != 1) return MOE_ERR_SHAPE;
@@ -99,10 +99,10 @@ int moe_suggest_block_m(int64_t num_tokens, int32_t topk, int32_t num_experts, i
     if (num_tokens < 0 || num_tokens >= (1ll << 40) || topk < 1 || topk > kMaxTopk || num_experts < 1)
         return MOE_ERR_SHAPE;
     // target rows = imbalance factor 2 x expected rows per expert (T * k / E); the smallest routing
-    // block that holds the target, compared exactly in integers: 2 T k <= c E
+    // block of the pages' ladder that holds the target, compared exactly in integers: 2 T k <= c E
     const int64_t twice_hits = 2 * num_tokens * topk;
-    int32_t pick = 128;
-    for (const int32_t c : {16, 32, 64, 128})
+    int32_t pick = kBlockLadder[kBlockLadderSize - 1];
+    for (const int32_t c : kBlockLadder)
         if (twice_hits <= (int64_t)c * num_experts) {
             pick = c;
             break;

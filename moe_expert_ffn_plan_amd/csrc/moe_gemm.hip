@@ -86,7 +86,8 @@ struct GemmArgs {
     uint8_t* out_sf;        // Linear1: per-block scales [cap/bm][N/256][bm][4]
     uint16_t* out_bf16;     // Linear2: [cap, N]
     int K, N, topk;
-    int bm_shift;           // log2 of the routing block (bm) that the scale layout uses
+    int bm;                 // the routing block (block_m) that the scale layout uses
+    int bm_shift;           // log2(bm) when bm is a power of two, else -1
     float swiglu_limit;     // Linear1: > 0 clamps gate from above and up on both sides before SwiGLU
     int exact_silu;         // Linear1: 1 = accurate expf and IEEE division in SiLU
     int count_idx;          // scalars[count_idx] = tiles in the list
@@ -247,17 +248,18 @@ __device__ __forceinline__ bool tile_of_block(const GemmArgs& g, int BN, TileId&
 }
 
 // Byte offset of row r's scale word of K-step 0 in the per-block layout
-// [cap/bm][KT][bm][4]; K-step kt adds kt * bm * 4.
-__device__ __forceinline__ uint32_t block_scale_offset(int r, int KT, int bm_shift) {
-    const int bm = 1 << bm_shift;
-    return (uint32_t)((((r >> bm_shift) * KT) << bm_shift) + (r & (bm - 1))) * 4u;
+// [cap/bm][KT][bm][4]; K-step kt adds kt * bm * 4.  bm_shift = log2(bm) for a power of two, else -1
+// (blocks of 96 and 192 rows divide).
+__device__ __forceinline__ uint32_t block_scale_offset(int r, int KT, int bm, int bm_shift) {
+    const int blk = bm_shift >= 0 ? r >> bm_shift : r / bm;
+    return (uint32_t)((blk * KT) * bm + (r - blk * bm)) * 4u;
 }
 // The same for K-step kt of row m0 + row_local, m0 the first row of a tile:
 // without PARTIAL the tile is one block of BM rows and m0 a multiple of BM.
 template <int BM, bool PARTIAL>
-__device__ __forceinline__ uint32_t tile_scale_offset(int m0, int row_local, int KT, int kt, int bm_shift) {
+__device__ __forceinline__ uint32_t tile_scale_offset(int m0, int row_local, int KT, int kt, int bm, int bm_shift) {
     if constexpr (PARTIAL)
-        return block_scale_offset(m0 + row_local, KT, bm_shift) + ((uint32_t)kt << (bm_shift + 2));
+        return block_scale_offset(m0 + row_local, KT, bm, bm_shift) + (uint32_t)(kt * bm) * 4u;
     else
         return (((uint32_t)m0 / BM * (uint32_t)KT + (uint32_t)kt) * BM + (uint32_t)row_local) * 4u;
 }
@@ -332,8 +334,8 @@ struct StageDma {
             sa_off = (uint32_t)(t >= 0 ? t : 0) * (uint32_t)(g.K / 32);
             sa_kt = 4;
         } else {   // per-block layout [cap/bm][KT][bm][4]
-            sa_off = block_scale_offset(m0 + (sa_row < rows ? sa_row : 0), KT, g.bm_shift);
-            sa_kt = 4 << g.bm_shift;
+            sa_off = block_scale_offset(m0 + (sa_row < rows ? sa_row : 0), KT, g.bm, g.bm_shift);
+            sa_kt = 4 * g.bm;
         }
     }
     __device__ __forceinline__ void init_b(const GemmArgs& g, const TileId& t, int bw_, int bnw_) {
@@ -360,8 +362,8 @@ struct StageDma {
     // blocks below the M-tile (block_m < 128: batches with few rows per expert, whose weight tiles serve
     // one or two M-tiles) stream them non-temporally: measured, the decode shape's GEMMs ran 13% faster,
     // prefill's 4% (its combine too, the slot rows staying cached), a 1024-token decode batch 8%.  With
-    // block_m = 128 the hint cost 2-6% where experts span many M-tiles, and choosing it per tile at run
-    // time cost 2-3% in the issue path itself.
+    // block_m >= 128 the hint cost 2-6% where experts span many M-tiles, and choosing it per tile at
+    // run time cost 2-3% in the issue path itself.
     template <int NB, int OFF>
     __device__ __forceinline__ void issue_b_blocks(uint8_t* st, int kt, int lane) const {
 #pragma unroll
@@ -506,7 +508,7 @@ __device__ __forceinline__ void epilogue_linear1(const v4f (&acc)[MI][NI], const
         if ((j & ((1 << VSHIFT) - 1)) == 0 && (!PARTIAL || own_row < rows)) {
             const int gcol = gcol0 + own_grp * 64;  // first Z column of the 32-channel group
             // Linear2 K-step = 256-column block of Z, byte = 64-column group within it
-            uint8_t* sp = g.out_sf + tile_scale_offset<BM, PARTIAL>(m0, own_row, ksteps2, gcol / kTileN, g.bm_shift) +
+            uint8_t* sp = g.out_sf + tile_scale_offset<BM, PARTIAL>(m0, own_row, ksteps2, gcol / kTileN, g.bm, g.bm_shift) +
                           (uint32_t)((gcol % kTileN) / 64);
             if constexpr (COHERENT) __hip_atomic_store(sp, (uint8_t)code, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             else *sp = (uint8_t)code;
@@ -580,6 +582,18 @@ __device__ __forceinline__ void load_row_tables(const GemmArgs& g, const TileId&
     __syncthreads();
 }
 
+// Tile variants of the kernels.  kTileFull: every tile is one routing block of BM rows.  The other two
+// cut an expert's padded rows into tiles of up to BM rows that can end early: kTileShortStream for
+// routing blocks below the M-tile (batches with few rows per expert, whose weight tiles serve one or two
+// M-tiles: the weights are streamed with the non-temporal hint, see issue_b_blocks), kTileShortCached for
+// routing blocks above it (192 rows: experts span many M-tiles, which reuse the weight tiles from the
+// caches, where the hint measured 2-6% slower).
+constexpr int kTileFull = 0, kTileShortStream = 1, kTileShortCached = 2;
+template <int TV>
+constexpr bool kPartial = TV != kTileFull;
+template <int BM, int TV>
+constexpr bool kStream = BM == 16 || TV == kTileShortStream;
+
 // ============================================================================
 // 256-column tiles: one group of 4 waves; per K-step wait, read, multiply.
 template <int BM>
@@ -597,8 +611,9 @@ struct Cfg4 {
     static_assert(2 * D < 64, "vmcnt range");
 };
 
-template <int BM, bool L1, bool PARTIAL, int EPI>
+template <int BM, bool L1, int TV, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
+    constexpr bool PARTIAL = kPartial<TV>;
     using C = Cfg4<BM>;
     using L = typename C::L;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[L::NS * L::STAGE];
@@ -613,7 +628,7 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmArgs g) {
     const int KT = g.K / kBK;
     load_row_tables<BM, L1>(g, t, row_w, row_tok, tid);
 
-    StageDma<BM, 256, C::A_PW, C::B_PW, BM == 16 || PARTIAL> dma;
+    StageDma<BM, 256, C::A_PW, C::B_PW, kStream<BM, TV>> dma;
     dma.init_a(g, t.m, t.rows, row_tok, L1, w, 4);
     dma.init_b(g, t, w, 4);
     auto issue = [&](int kt) {
@@ -766,9 +781,10 @@ struct TileSeq {
 };
 
 // One persistent run over the tiles `seq` of g's list.
-template <int BM, bool L1, bool PARTIAL, bool FUSED, int EPI>
+template <int BM, bool L1, int TV, bool FUSED, int EPI>
 __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync, const TileSeq& seq,
                                        PPShared<BM>& sh) {
+    constexpr bool PARTIAL = kPartial<TV>;
     const int ntiles = seq.n;
     using C = CfgPP<BM, L1, FUSED>;
     using L = typename C::L;
@@ -829,7 +845,7 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
     wait_and_barrier<0>();
 
     if (grp == 0) {
-        StageDma<BM, 512, 1, C::B0_PW, BM == 16 || PARTIAL> dma;
+        StageDma<BM, 512, 1, C::B0_PW, kStream<BM, TV>> dma;
         dma.init_b(g, t0, wq, 4);
         // stage s (and the table load that rides with it) for compute step gs = s - (NS - 1)
         auto issue = [&](int s) {
@@ -877,7 +893,7 @@ __device__ __forceinline__ void pp_run(const GemmArgs& g, const FusedSync& sync,
         deferred_epilogue();
         if constexpr (FUSED) __syncthreads();  // B_S
     } else {
-        StageDma<BM, 512, C::A_PW, 1, BM == 16 || PARTIAL> dma;
+        StageDma<BM, 512, C::A_PW, 1, kStream<BM, TV>> dma;
         // fused Linear2: before the activation DMA of K-step kt of tile j, wait until the Linear1 tile
         // that wrote those channels of t's rows is done.  Linear2 K-step kt reads h channels
         // [128 kt, 128 kt + 128), which Linear1 N-tile kt / 2 (256 SwiGLU channels, 512 gate/up
@@ -1002,7 +1018,7 @@ __device__ __forceinline__ TileSeq round_robin(int begin, int end, int slot, int
     return TileSeq{first, n, nslots, 0, 1, n};
 }
 
-template <int BM, bool L1, bool PARTIAL, int EPI>
+template <int BM, bool L1, int TV, int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
     __shared__ PPShared<BM> sh;
     if (L1 && g.status && blockIdx.x == 0 && threadIdx.x == 0) *g.status = 0u;
@@ -1010,7 +1026,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(GemmArgs g) {
     xcd_chunk(g, g.N / 512, blockIdx.x % kNumXcd, begin, end);
     const TileSeq seq = round_robin(begin, end, blockIdx.x / kNumXcd, gridDim.x / kNumXcd);
     if (seq.n == 0) return;
-    pp_run<BM, L1, PARTIAL, false, EPI>(g, FusedSync{}, seq, sh);
+    pp_run<BM, L1, TV, false, EPI>(g, FusedSync{}, seq, sh);
 }
 
 struct FusedArgs {
@@ -1042,7 +1058,7 @@ __global__ void fused_prepare_kernel(uint32_t* epoch_word, uint32_t* status) {
 // light workgroups run the first L * d Linear2 tiles (d = Linear2 tiles per Linear1 tile of time,
 // from the K-steps; the list runs M-tile by M-tile, so these need the M-tiles the first Linear1
 // round computed); the rest go round-robin to all workgroups.
-template <int BM, bool PARTIAL, int EPI>
+template <int BM, int TV, int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_fused_kernel(FusedArgs fa) {
     __shared__ PPShared<BM> sh;
     const int nslots = gridDim.x / kNumXcd, xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
@@ -1054,7 +1070,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fused_kernel(FusedArgs fa) {
     xcd_chunk(fa.g1, fa.g1.N / 512, xcd, b1, e1);
     xcd_chunk(fa.g2, fa.g2.N / 512, xcd, b2, e2);
     const TileSeq s1 = round_robin(b1, e1, slot, nslots);
-    if (s1.n > 0) pp_run<BM, true, PARTIAL, true, EPI>(fa.g1, sync, s1, sh);
+    if (s1.n > 0) pp_run<BM, true, TV, true, EPI>(fa.g1, sync, s1, sh);
     wait_and_barrier<0>();  // the Linear1 run's table loads have landed before the tables are reused
 
     const int r1 = (e1 - b1) % nslots, nl = r1 > 0 ? nslots - r1 : 0;  // light workgroups: slots >= r1
@@ -1069,7 +1085,7 @@ __global__ __launch_bounds__(512, 1) void gemm_fused_kernel(FusedArgs fa) {
     s2.first_b = b2 + na_all + slot;
     s2.stride_b = nslots;
     s2.n = s2.n_a + (s2.first_b < e2 ? (e2 - s2.first_b + nslots - 1) / nslots : 0);
-    if (s2.n > 0) pp_run<BM, false, PARTIAL, true, kEpiFast>(fa.g2, sync, s2, sh);
+    if (s2.n > 0) pp_run<BM, false, TV, true, kEpiFast>(fa.g2, sync, s2, sh);
 }
 
 // Compute units of the current device (cached per device).
@@ -1099,13 +1115,13 @@ int64_t persistent_grid(int64_t all) {
     return std::max<int64_t>(kNumXcd, std::min(all, cus));
 }
 
-template <int BM, bool L1, bool PARTIAL, int EPI>
+template <int BM, bool L1, int TV, int EPI>
 hipError_t launch_bm_epi(const GemmArgs& args, int64_t all, hipStream_t stream) {
     if (gemm_bn(args.N) == 512) {
         const int64_t grid = args.K / kBK >= min_kt_persistent(BM) ? persistent_grid(all) : all;
-        hipLaunchKernelGGL((gemm_pp_kernel<BM, L1, PARTIAL, EPI>), dim3(grid), dim3(512), 0, stream, args);
+        hipLaunchKernelGGL((gemm_pp_kernel<BM, L1, TV, EPI>), dim3(grid), dim3(512), 0, stream, args);
     } else {
-        hipLaunchKernelGGL((gemm4_kernel<BM, L1, PARTIAL, EPI>), dim3(all), dim3(256), 0, stream, args);
+        hipLaunchKernelGGL((gemm4_kernel<BM, L1, TV, EPI>), dim3(all), dim3(256), 0, stream, args);
     }
     return hipGetLastError();
 }
@@ -1113,51 +1129,49 @@ hipError_t launch_bm_epi(const GemmArgs& args, int64_t all, hipStream_t stream) 
 // Linear1 epilogue variant of a problem
 int epi_of(const GemmArgs& a) { return a.exact_silu ? kEpiExact : a.swiglu_limit > 0.0f ? kEpiClamp : kEpiFast; }
 
-template <int BM, bool PARTIAL>
+template <int BM, int TV>
 void launch_fused(int epi, dim3 grid, dim3 block, hipStream_t stream, const FusedArgs& fa) {
-    if (epi == kEpiClamp) hipLaunchKernelGGL((gemm_fused_kernel<BM, PARTIAL, kEpiClamp>), grid, block, 0, stream, fa);
-    else if (epi == kEpiExact) hipLaunchKernelGGL((gemm_fused_kernel<BM, PARTIAL, kEpiExact>), grid, block, 0, stream, fa);
-    else hipLaunchKernelGGL((gemm_fused_kernel<BM, PARTIAL, kEpiFast>), grid, block, 0, stream, fa);
+    if (epi == kEpiClamp) hipLaunchKernelGGL((gemm_fused_kernel<BM, TV, kEpiClamp>), grid, block, 0, stream, fa);
+    else if (epi == kEpiExact) hipLaunchKernelGGL((gemm_fused_kernel<BM, TV, kEpiExact>), grid, block, 0, stream, fa);
+    else hipLaunchKernelGGL((gemm_fused_kernel<BM, TV, kEpiFast>), grid, block, 0, stream, fa);
 }
 
 // all: workgroups for one tile each
-template <int BM, bool L1, bool PARTIAL>
+template <int BM, bool L1, int TV>
 hipError_t launch_bm(const GemmArgs& args, int64_t all, hipStream_t stream) {
     if constexpr (L1) {
         switch (epi_of(args)) {
-            case kEpiClamp: return launch_bm_epi<BM, true, PARTIAL, kEpiClamp>(args, all, stream);
-            case kEpiExact: return launch_bm_epi<BM, true, PARTIAL, kEpiExact>(args, all, stream);
-            default: return launch_bm_epi<BM, true, PARTIAL, kEpiFast>(args, all, stream);
+            case kEpiClamp: return launch_bm_epi<BM, true, TV, kEpiClamp>(args, all, stream);
+            case kEpiExact: return launch_bm_epi<BM, true, TV, kEpiExact>(args, all, stream);
+            default: return launch_bm_epi<BM, true, TV, kEpiFast>(args, all, stream);
         }
     }
-    return launch_bm_epi<BM, L1, PARTIAL, kEpiFast>(args, all, stream);
+    return launch_bm_epi<BM, L1, TV, kEpiFast>(args, all, stream);
 }
 
 // Workgroups for one tile each of a GEMM with N columns: every XCD gets the slots of ceil(M-tiles / 8)
-// M-tiles (xcd_chunk), for an upper bound on the M-tiles (the padded rows are not known on the host:
-// every M-tile but each expert's last covers bmg / bm whole blocks).
+// M-tiles (xcd_chunk), for an upper bound on the M-tiles (the padded rows are not known on the host).
 int64_t one_tile_grid(const GemmProblem& p, int N) {
-    const int bm = p.shape->block_m, bmg = gemm_bm(bm);
-    const int64_t blocks = p.cap / bm;
-    const int64_t mtiles = std::min<int64_t>(blocks, blocks / (bmg / bm) + p.shape->num_experts);
+    const int64_t mtiles = max_m_tiles(*p.shape);
     return kNumXcd * ((mtiles + kNumXcd - 1) / kNumXcd) * (N / gemm_bn(N));
 }
 
 template <bool L1>
 hipError_t launch_gemm(const GemmProblem& p, GemmArgs args, hipStream_t stream) {
     const int bm = p.shape->block_m, bmg = gemm_bm(bm);
-    args.bm_shift = 31 - __builtin_clz((unsigned)bm);
     const int64_t tiles = one_tile_grid(p, args.N);
     if (tiles == 0) return hipSuccess;
     if (bmg == bm) {
         switch (bmg) {
-            case 16: return launch_bm<16, L1, false>(args, tiles, stream);
-            case 128: return launch_bm<128, L1, false>(args, tiles, stream);
+            case 16: return launch_bm<16, L1, kTileFull>(args, tiles, stream);
+            case 128: return launch_bm<128, L1, kTileFull>(args, tiles, stream);
             default: return hipErrorInvalidValue;
         }
     }
     switch (bmg) {
-        case 128: return launch_bm<128, L1, true>(args, tiles, stream);
+        case 128:
+            if (bm < bmg) return launch_bm<128, L1, kTileShortStream>(args, tiles, stream);
+            return launch_bm<128, L1, kTileShortCached>(args, tiles, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1168,7 +1182,8 @@ GemmArgs common_args(const GemmProblem& p) {
     a.row_token = p.plan->row_token;
     a.row_topk = p.plan->row_topk;
     a.topk = p.shape->topk;
-    a.bm_shift = 31 - __builtin_clz((unsigned)p.shape->block_m);
+    a.bm = p.shape->block_m;
+    a.bm_shift = (a.bm & (a.bm - 1)) == 0 ? 31 - __builtin_clz((unsigned)a.bm) : -1;
     a.swiglu_limit = p.shape->swiglu_limit;
     a.exact_silu = p.shape->exact_silu;
     return a;
@@ -1243,9 +1258,10 @@ hipError_t launch_expert_ffn(const GemmProblem& p, const uint8_t* x, const uint8
     hipLaunchKernelGGL(fused_prepare_kernel, dim3(1), dim3(64), 0, stream, epoch_word, status);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (bmg == 16) launch_fused<16, false>(epi, grid, block, stream, fa);
-    else if (bm == 128) launch_fused<128, false>(epi, grid, block, stream, fa);
-    else launch_fused<128, true>(epi, grid, block, stream, fa);
+    if (bmg == 16) launch_fused<16, kTileFull>(epi, grid, block, stream, fa);
+    else if (bm == 128) launch_fused<128, kTileFull>(epi, grid, block, stream, fa);
+    else if (bm < 128) launch_fused<128, kTileShortStream>(epi, grid, block, stream, fa);
+    else launch_fused<128, kTileShortCached>(epi, grid, block, stream, fa);
     return hipGetLastError();
 }
 

@@ -22,10 +22,21 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Routing of large inputs runs as three kernels over groups of kRouteTokensPerGroup tokens.
 constexpr int kRouteTokensPerGroup = 64;
 
+// Routing blocks (block_m) the library takes: the walk-through's BLOCK_M candidates (section 7.1).
+constexpr int kBlockLadder[] = {16, 32, 64, 96, 128, 192};
+constexpr int kBlockLadderSize = 6;
+inline bool block_m_supported(int bm) {
+    for (const int c : kBlockLadder)
+        if (bm == c) return true;
+    return false;
+}
+
 // Tile widths of the two GEMMs: 512 columns when N allows it, else 256.
 inline int gemm_bn(int n) { return n % 512 == 0 ? 512 : 256; }
-// GEMM M-tile: up to 128 rows (several block_m blocks of one expert) once block_m >= 32; for smaller
-// block_m (decode-sized batches, a block or two per expert) the tile is one block.
+// GEMM M-tile: up to 128 rows of one expert once block_m >= 32 (several blocks, part of one, or, with
+// blocks of 96 and 192 rows, spans that cross block boundaries: an expert's padded rows are cut into
+// tiles of 128 from its first row, the last one shorter); for smaller block_m (decode-sized batches, a
+// block or two per expert) the tile is one block.
 inline int gemm_bm(int block_m) { return block_m >= 32 ? 128 : block_m; }
 // Rows past `cap` that the row tables reserve, so a 128-row tile starting at the last block reads
 // allocated memory (the GEMMs mask every row past the tile's valid count).
@@ -49,6 +60,12 @@ inline int64_t capacity_rows(const moe_shape& s) {
     return (raw + s.block_m - 1) / s.block_m * s.block_m;
 }
 
+// Upper bound on the GEMM M-tiles of a routing: expert e has ceil(padded_e / bmg) of them, so at most
+// R_pad / bmg + E over all experts, R_pad <= cap.
+inline int64_t max_m_tiles(const moe_shape& s) {
+    return (capacity_rows(s) + gemm_bm(s.block_m) - 1) / gemm_bm(s.block_m) + s.num_experts;
+}
+
 inline PlanLayout plan_layout(const moe_shape& s) {
     PlanLayout L;
     L.cap = capacity_rows(s);
@@ -66,13 +83,12 @@ inline PlanLayout plan_layout(const moe_shape& s) {
     L.pull_order = take((size_t)s.num_tokens * 4);
     L.groups = (s.num_tokens + kRouteTokensPerGroup - 1) / kRouteTokensPerGroup;
     L.group_counts = take((size_t)L.groups * s.num_experts * 2 * 4);  // hit and pull counts per group
-    // GEMM tile lists: tile = (expert, M-tile, N-tile), expert by expert, for each N-tile all M-tiles;
-    // every M-tile covers at least one block, so max_blocks M-tiles bound the count
+    // GEMM tile lists: tile = (expert, M-tile, N-tile), M-tile by M-tile, all N-tiles of each
     L.bmg = gemm_bm(s.block_m);
     L.nt1 = 2 * s.intermediate / gemm_bn(2 * s.intermediate);
     L.nt2 = s.hidden / gemm_bn(s.hidden);
-    L.max_tiles1 = L.max_blocks * L.nt1;
-    L.max_tiles2 = L.max_blocks * L.nt2;
+    L.max_tiles1 = max_m_tiles(s) * L.nt1;
+    L.max_tiles2 = max_m_tiles(s) * L.nt2;
     L.tiles1 = take((size_t)L.max_tiles1 * kTileWords * 4);
     L.tiles2 = take((size_t)L.max_tiles2 * kTileWords * 4);
     L.total = o;

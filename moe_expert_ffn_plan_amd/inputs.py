@@ -23,8 +23,8 @@ Workloads (one GPU's share each; expert ids are global, experts
 * ``dsv4``     one rank's share of the DeepSeek-V4 expert shape the reading
   notes' tests use: 8 ranks x 8192 tokens = 65536 tokens routed, hidden
   7168, intermediate 3072, 48 local of 384 experts, top-6 distinct uniform,
-  Dirichlet(1) weights; block_m 128 (the pages' 192 is not a supported
-  block; 128 is what the block heuristic picks for this shape).
+  Dirichlet(1) weights; block_m 192, the pages' block for this test (and
+  what the block heuristic picks for the shape).
 
 Values: x ~ N(0, 1); weights ~ N(0, std = 1/sqrt(K)) with K the reduction
 size of that GEMM.  Both are quantised per 32 consecutive K elements with a
@@ -65,7 +65,7 @@ WORKLOADS = {
     "prefill": Workload("prefill", 4096, 7168, 2048, 32, 256, 8, 32, "uniform", seed=1003, weight_seed=2002),
     "skewed": Workload("skewed", 16384, 7168, 2048, 32, 256, 8, 128, "zipf", 0.1, 50.0, seed=1004,
                        weight_seed=2002),
-    "dsv4": Workload("dsv4", 65536, 7168, 3072, 48, 384, 6, 128, "uniform", seed=1005, weight_seed=2005),
+    "dsv4": Workload("dsv4", 65536, 7168, 3072, 48, 384, 6, 192, "uniform", seed=1005, weight_seed=2005),
 }
 ORDER = ["tiny", "tp_slice", "decode", "prefill", "skewed", "dsv4"]
 

@@ -121,6 +121,10 @@ SMALL = {
                                    weight_seed=24),
     "small_skewed": inputs.Workload("small_skewed", 1500, 1024, 256, 8, 64, 8, 128, "zipf", 0.1, 50.0, seed=15,
                                     weight_seed=25),
+    # blocks of 96 and 192 rows: 128-row M-tiles cut across block boundaries, one launch and two
+    "small_bm96": inputs.Workload("small_bm96", 900, 1024, 512, 6, 8, 4, 96, "uniform", seed=18, weight_seed=28),
+    "small_bm192": inputs.Workload("small_bm192", 1300, 1024, 640, 5, 7, 6, 192, "zipf", 0.1, 50.0, seed=19,
+                                   weight_seed=29),
 }
 
 

@@ -1,7 +1,7 @@
 """Seeded random shapes through the whole forward (moe_plan + moe_forward), each compared in full
 with the CPU oracle: routing tables bit-exact, FP8 intermediates and y within the parity gates.
 
-The draws cover every routing block (16, 32, 64, 128), hidden and intermediate sizes that select
+The draws cover every routing block (16, 32, 64, 96, 128, 192), hidden and intermediate sizes that select
 either GEMM schedule (one persistent launch or two; 512- or 256-column tiles), one to sixteen local
 experts out of up to four times as many, top-1 to top-8 with uniform or Zipf routing, a shifted
 range of local expert ids, a few tokens up to a few hundred, the activation clamp and the accurate
@@ -35,7 +35,7 @@ def fuzz_case(i):
     G = int(r.integers(E, 4 * E + 1))
     k = int(r.integers(1, min(8, G) + 1))
     T = int(r.choice([1, 2, 7, 63, 64, 65, 130, 257, 411]))
-    bm = int(r.choice([16, 32, 64, 128]))
+    bm = int(r.choice([16, 32, 64, 96, 128, 192]))
     routing = str(r.choice(["uniform", "zipf"]))
     outliers = float(r.choice([0.0, 0.1]))
     begin = int(r.choice([0, G - E]))

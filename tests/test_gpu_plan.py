@@ -87,13 +87,25 @@ def test_plan_path_boundary(gpu, T, k, E):
     assert_plan_equal(g, plan_ref(ids, E, 0, 32))
 
 
+@pytest.mark.parametrize("bm", [96, 192])
+@pytest.mark.parametrize("T,k,E", [(300, 8, 40), (4096, 8, 64), (20000, 6, 48), (9000, 8, 512)])
+def test_plan_blocks_96_192(gpu, bm, T, k, E):
+    """The two routing blocks of the ladder that are not powers of two, through every routing path
+    (one workgroup; counts + fused scan; counts, scan, scatter for the largest group x expert table)."""
+    rng = np.random.default_rng(T + 7 * bm + E)
+    ids = rng.integers(-2, E + 5, size=(T, k))
+    print(f"plan block {bm}: T={T} k={k} E={E}", flush=True)
+    (g,) = gpu_plan(ids, E, bm, 0, gpu)
+    assert_plan_equal(g, plan_ref(ids, E, 0, bm))
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_plan_fuzz(gpu, seed):
     rng = np.random.default_rng(100 + seed)
     T = int(rng.integers(1, 9000))
     k = int(rng.integers(1, 10))
     E = int(rng.integers(1, 100))
-    bm = int(rng.choice([16, 32, 64, 128]))
+    bm = int(rng.choice([16, 32, 64, 96, 128, 192]))
     begin = int(rng.integers(0, 50))
     ids = rng.integers(begin - 3, begin + 2 * E, size=(T, k))
     print(f"plan fuzz seed {seed}: T={T} k={k} E={E} bm={bm} begin={begin}", flush=True)

@@ -46,7 +46,7 @@ def test_capacity_matches_oracle(T, H, I, E, k, bm):
 
 
 @pytest.mark.parametrize("bad,status", [
-    (dict(block_m=48), -2), (dict(block_m=8), -2), (dict(num_experts=0), -2), (dict(num_experts=513), -2),
+    (dict(block_m=48), -2), (dict(block_m=8), -2), (dict(block_m=256), -2), (dict(block_m=160), -2), (dict(num_experts=0), -2), (dict(num_experts=513), -2),
     (dict(topk=0), -2), (dict(topk=65), -2), (dict(num_tokens=-1), -2), (dict(hidden=384), -3),
     (dict(intermediate=192), -3), (dict(hidden=0), -2)])
 def test_shape_validation(bad, status):
@@ -55,6 +55,14 @@ def test_shape_validation(bad, status):
     s = B.make_shape(**kw)
     v = ctypes.c_size_t()
     assert B.lib().moe_forward_workspace_bytes(ctypes.byref(s), ctypes.byref(v)) == status
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64, 96, 128, 192])
+def test_block_m_ladder_accepted(bm):
+    """Every routing block of the walk-through's BLOCK_M candidates is a valid shape."""
+    s = B.make_shape(200, 512, 256, 6, 4, bm)
+    assert B.capacity_rows(s) == capacity_rows(200, 4, 6, bm)
+    assert B.capacity_rows(s) % bm == 0
 
 
 def test_null_and_empty_inputs_return_before_gpu_work():
@@ -77,19 +85,23 @@ def test_misaligned_and_small_workspace():
 
 
 # Routing block heuristic (walk-through section 7.1, "BLOCK_M selection"): target = 2 (imbalance
-# factor) x expected rows per expert, expected = tokens x topk / experts; the smallest supported block
-# (16, 32, 64, 128) that holds the target, else 128.  Each case states its target.
+# factor) x expected rows per expert, expected = tokens x topk / experts; the smallest candidate of the
+# ladder (16, 32, 64, 96, 128, 192) that holds the target, else 192.  Each case states its target.
 @pytest.mark.parametrize("T,k,E,want", [
     (128, 8, 256, 16),     # decode: expected 4, target 8
     (256, 8, 256, 16),     # target exactly 16: equality keeps the smaller block
     (257, 8, 256, 32),     # target 16.06
     (512, 8, 256, 32),     # target 32
     (1024, 8, 256, 64),    # target 64
-    (1025, 8, 256, 128),   # target 64.06
+    (1025, 8, 256, 96),    # target 64.06
+    (1536, 8, 256, 96),    # target exactly 96
+    (1537, 8, 256, 128),   # target 96.06
     (2048, 8, 256, 128),   # target 128
-    (4096, 8, 256, 128),   # prefill: target 256, above the ladder
-    (2048, 8, 64, 128),    # TP slice: target 512
-    (8 * 8192, 6, 384, 128),  # DeepSeek-V4 test shape, 8 ranks x 8192 tokens, top-6 of 384: target 2048
+    (2049, 8, 256, 192),   # target 128.06
+    (3072, 8, 256, 192),   # target exactly 192
+    (4096, 8, 256, 192),   # prefill: target 256, above the ladder
+    (2048, 8, 64, 192),    # TP slice: target 512
+    (8 * 8192, 6, 384, 192),  # DeepSeek-V4 test shape, 8 ranks x 8192 tokens, top-6 of 384: target 2048
     (64, 2, 8, 32),        # tiny: expected 16, target 32
     (0, 8, 256, 16),       # no tokens: the smallest block
     (1, 1, 1, 16),         # target 2
@@ -102,10 +114,11 @@ def test_suggest_block_m_ladder_properties():
     prev = 16
     for T in range(0, 5000, 7):
         bm = B.suggest_block_m(T, 8, 256)
-        assert bm in (16, 32, 64, 128) and bm >= prev  # one of the blocks, never smaller with more tokens
+        ladder = (16, 32, 64, 96, 128, 192)
+        assert bm in ladder and bm >= prev  # one of the blocks, never smaller with more tokens
         target = 2 * T * 8 / 256
-        assert bm >= target or bm == 128
-        assert bm == 16 or bm // 2 < target  # the smallest block that holds the target
+        assert bm >= target or bm == 192
+        assert bm == 16 or ladder[ladder.index(bm) - 1] < target  # the smallest block that holds the target
         prev = bm
 
 
@@ -131,7 +144,8 @@ def _launch_rule(T, H, I, E, k, bm, cus=256):
     (2048, 4096, 768, 64, 8, 128), (128, 7168, 2048, 32, 8, 16), (4096, 7168, 2048, 32, 8, 32),
     (16384, 7168, 2048, 32, 8, 128), (64, 256, 128, 8, 2, 128), (400, 1024, 256, 5, 3, 64),
     (300, 1024, 768, 10, 6, 16), (65536, 7168, 3072, 48, 6, 128), (4096, 7168, 2048, 32, 8, 128),
-    (8192, 7168, 2048, 32, 8, 32), (100, 7168, 2048, 32, 8, 16)])
+    (8192, 7168, 2048, 32, 8, 32), (100, 7168, 2048, 32, 8, 16), (65536, 7168, 3072, 48, 6, 192),
+    (4096, 7168, 2048, 32, 8, 96), (700, 1024, 512, 7, 5, 192)])
 def test_gemm_launches_rule(T, H, I, E, k, bm):
     s = B.make_shape(T, H, I, E, k, bm)
     cus = 256
