@@ -15,7 +15,11 @@ moe_expert_ffn, both GEMMs in one persistent launch, or moe_linear1 and
 moe_linear2, as moe_gemm_launches reports; moe_combine); they are issued one by one so HIP
 events on that stream can bracket the dominant GEMM launch inside the timed
 steps (the roofline's achieved rate).  --staged and --expert-ffn force one
-schedule or the other.  Three copies of the
+schedule or the other.  By default every timed step is recorded as three HIP
+graphs (the calls before the dominant GEMM launch, that launch, the calls
+after it) and the timed loop replays them, recording the events around the
+dominant launch between the replays; --launch stream issues the calls one by
+one instead.  Three copies of the
 expert weights are rotated between steps so they stream from HBM rather than
 the 256 MB Infinity Cache.  The default warmup (50 steps) lets the clocks
 settle; the first steps after idle run ~15% slower.
@@ -31,6 +35,7 @@ oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import dataclasses
 import hashlib
 import json
@@ -44,6 +49,55 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer useful TFLOP/s + tokens/s at 1 GPU; % of scaled-MFMA peak / HBM BW"
 PEAK_MFMA_TFLOPS = 5000.0      # MI355X dense FP8 MFMA; FP8 x FP4 scaled MFMA issues at this rate
 PEAK_HBM_GBS = 8000.0
+
+
+class DeviceEvents:
+    """HIP events created with hipEventDisableSystemFence, for timing only.  A default event performs a
+    system-scope memory fence when it completes (a writeback and invalidation of the caches), which on
+    this GPU costs the kernels that follow it time; these events record the timestamp without it.  They
+    come from the HIP runtime torch has loaded, so torch's stream handles are valid for them."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventRecordWithFlags.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def new(self):
+        e = ctypes.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.events.append(e)
+        return e
+
+    def record(self, e, stream):
+        """Record on `stream`; while the stream is being captured into a graph, as an event node of the
+        graph (hipEventRecordExternal), so that every replay records it."""
+        import torch
+        if torch.cuda.is_current_stream_capturing():
+            rc = self.hip.hipEventRecordWithFlags(e, ctypes.c_void_p(stream.cuda_stream), 1)
+        else:
+            rc = self.hip.hipEventRecord(e, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a, b) -> float:
+        """Milliseconds between two recorded events; the stream must have been synchronized."""
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
 
 
 def kernel_traffic(kind: str, workload: str):
@@ -129,8 +183,10 @@ def main() -> int:
                     help="run Linear1 and Linear2 through moe_expert_ffn (one launch) wherever it is supported")
     ap.add_argument("--host-inputs", action="store_true",
                     help="draw the synthetic inputs on the CPU and copy them (fewer torch GPU kernels, for profilers)")
-    ap.add_argument("--graph", action="store_true",
-                    help="record each step (one per weight copy) into a HIP graph and time graph replays")
+    ap.add_argument("--launch", choices=("graph", "stream"), default="graph",
+                    help="graph (default): every timed step recorded as HIP graphs (the calls before the dominant "
+                         "GEMM launch, that launch, the calls after it) and timed as their replays; stream: the "
+                         "library calls issued on the stream step by step")
     ap.add_argument("--block-m", type=int, default=0,
                     help="routing block rows to use instead of the workload's own (16, 32, 64 or 128)")
     ap.add_argument("--tokens", type=int, default=0,
@@ -182,6 +238,7 @@ def main() -> int:
     ws = torch.empty(B.forward_workspace_bytes(s), dtype=torch.uint8, device=dev)
     y = torch.empty(w.num_tokens, w.hidden, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
+    dev_ev = DeviceEvents()
     # the schedule moe_forward picks (moe_gemm_launches): one persistent launch for both GEMMs while
     # Linear1 has few tiles per CU, else the two GEMM launches
     fused = B.forward_uses_expert_ffn(s) and B.expert_ffn_is_fused(s) and not args.staged
@@ -189,30 +246,36 @@ def main() -> int:
         fused = B.expert_ffn_is_fused(s)
     stages = ["plan", "expert_ffn", "combine"] if fused else ["plan", "linear1", "linear2", "combine"]
 
+    def calls(i, staged):
+        """The step's library calls in order, as (stage name, call on a stream); the dominant GEMM launch
+        is the one named linear1 or expert_ffn."""
+        wt = weights[i % len(weights)]
+        c = [("plan", lambda st: B.plan(s, d["topk_idx"], plan_ws, st))]
+        if staged:
+            c.append(("linear1", lambda st: B.linear1(s, d["x"], d["x_sf"], d["topk_w"], wt["w1"], wt["w1_sf"],
+                                                      plan_ws, ws, st)))
+            c.append(("linear2", lambda st: B.linear2(s, wt["w2"], wt["w2_sf"], plan_ws, ws, st)))
+        else:
+            c.append(("expert_ffn", lambda st: B.expert_ffn(s, d["x"], d["x_sf"], d["topk_w"], wt["w1"], wt["w1_sf"],
+                                                            wt["w2"], wt["w2_sf"], plan_ws, ws, st)))
+        c.append(("combine", lambda st: B.combine(s, plan_ws, ws, y, st)))
+        return c
+
     def step(i, events=None, k_events=None, staged=not fused):
         """One step; events: one per stage boundary; k_events: around the dominant GEMM launch."""
-        wt = weights[i % len(weights)]
-        stream = torch.cuda.current_stream()  # the capture stream while a graph is being recorded
-        rec = (lambda j: events[j].record(stream)) if events is not None else (lambda j: None)
-        rec(0)
-        B.plan(s, d["topk_idx"], plan_ws, stream)
-        rec(1)
-        if k_events is not None:
-            k_events[0].record(stream)
-        if staged:
-            B.linear1(s, d["x"], d["x_sf"], d["topk_w"], wt["w1"], wt["w1_sf"], plan_ws, ws, stream)
-            if k_events is not None:
-                k_events[1].record(stream)
-            rec(2)
-            B.linear2(s, wt["w2"], wt["w2_sf"], plan_ws, ws, stream)
-        else:
-            B.expert_ffn(s, d["x"], d["x_sf"], d["topk_w"], wt["w1"], wt["w1_sf"], wt["w2"], wt["w2_sf"], plan_ws,
-                         ws, stream)
-            if k_events is not None:
-                k_events[1].record(stream)
-        rec(3 if staged else 2)
-        B.combine(s, plan_ws, ws, y, stream)
-        rec(4 if staged else 3)
+        stream = torch.cuda.current_stream()
+        c = calls(i, staged)
+        for j, (name, call) in enumerate(c):
+            if events is not None:
+                dev_ev.record(events[j], stream)
+            dominant = k_events is not None and name in ("linear1", "expert_ffn")
+            if dominant:
+                dev_ev.record(k_events[0], stream)
+            call(stream)
+            if dominant:
+                dev_ev.record(k_events[1], stream)
+        if events is not None:
+            dev_ev.record(events[len(c)], stream)
 
     for i in range(args.warmup):
         step(i)
@@ -234,30 +297,40 @@ def main() -> int:
     check_status("warmup")
 
     # timed steps: wall time; HIP events bracket only the dominant GEMM launch (same stream)
-    k_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    if args.graph:
-        # one recorded step per weight copy; the timed loop replays them in turn, and the events around
-        # the dominant launch come from an eager pass right after
-        graphs = []
+    k_evs = [[dev_ev.new() for _ in range(2)] for _ in range(args.steps)]
+    if args.launch == "graph":
+        # every timed step as three recorded graphs (the calls before the dominant GEMM launch, that
+        # launch, the calls after it; the weight copies in turn): the events around the dominant launch
+        # are recorded between the replays, on the stream they replay on.  Each graph is replayed once
+        # untimed first.
         side = torch.cuda.Stream()
-        for c in range(len(weights)):
-            side.wait_stream(torch.cuda.current_stream())
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=side):
-                step(c)
-            graphs.append(g)
+        segs = []
+        for i in range(args.steps):
+            c = calls(i, not fused)
+            k = next(j for j, (name, _) in enumerate(c) if name in ("linear1", "expert_ffn"))
+            parts = []
+            for part in (c[:k], c[k:k + 1], c[k + 1:]):
+                side.wait_stream(torch.cuda.current_stream())
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    for _, call in part:
+                        call(torch.cuda.current_stream())
+                parts.append(g)
+            segs.append(parts)
         torch.cuda.synchronize()
-        for i in range(len(graphs) * 4):
-            graphs[i % len(graphs)].replay()
+        for parts in segs:
+            for g in parts:
+                g.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
-            graphs[i % len(graphs)].replay()
+        for i, (pre, dom, post) in enumerate(segs):
+            pre.replay()
+            dev_ev.record(k_evs[i][0], stream)
+            dom.replay()
+            dev_ev.record(k_evs[i][1], stream)
+            post.replay()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        for i in range(args.steps):
-            step(i, k_events=k_evs[i])
-        torch.cuda.synchronize()
     else:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -266,17 +339,18 @@ def main() -> int:
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
-    k_ms = sum(e[0].elapsed_time(e[1]) for e in k_evs) / args.steps
+    k_ms = sum(dev_ev.elapsed_ms(e[0], e[1]) for e in k_evs) / args.steps
     check_status("timed steps")
 
     # untimed breakdown passes: an event between every stage (and the two-launch path for comparison)
     def breakdown(staged):
         names = ["plan", "linear1", "linear2", "combine"] if staged else stages
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+        evs = [[dev_ev.new() for _ in range(len(names) + 1)] for _ in range(args.steps)]
         for i in range(args.steps):
             step(i, evs[i], staged=staged)
         torch.cuda.synchronize()
-        return {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, name in enumerate(names)}
+        return {name: sum(dev_ev.elapsed_ms(e[j], e[j + 1]) for e in evs) / args.steps
+                for j, name in enumerate(names)}
     kern_ms = breakdown(not fused)
     staged_ms = breakdown(True) if fused else None
 
@@ -312,7 +386,7 @@ def main() -> int:
            "config": {"workload": w.name, "tokens": w.num_tokens, "hidden": H, "intermediate": I,
                       "local_experts": w.num_experts, "topk": w.topk, "block_m": w.block_m,
                       "valid_rows": n_valid, "padded_rows": r_pad, "weight_copies": args.weight_copies,
-                      "launch": "graph" if args.graph else "stream"},
+                      "launch": args.launch},
            "tokens_per_s": round(w.num_tokens / (ms * 1e-3), 1),
            "pct_of_mfma_peak": round(100 * tflops / PEAK_MFMA_TFLOPS, 2),
            "pct_of_hbm_peak": round(100 * step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
