@@ -19,8 +19,16 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Offsets (bytes) of each table inside a plan workspace.
-// Routing of large inputs runs as three kernels over groups of kRouteTokensPerGroup tokens.
-constexpr int kRouteTokensPerGroup = 64;
+// Routing of large inputs runs over groups of route_group_tokens(T) tokens: 64, or 128 or 256 when
+// that keeps the groups to at most kRouteMaxGroups (each group of the fused scan reads the counts of
+// all groups, so their number must stay small).  A group's four waves take a quarter each, at most
+// one token per lane.
+constexpr int kRouteMaxGroups = 256;
+inline int route_group_tokens(int64_t num_tokens) {
+    int tpg = 64;
+    while (tpg < 256 && (num_tokens + tpg - 1) / tpg > kRouteMaxGroups) tpg *= 2;
+    return tpg;
+}
 
 // Routing blocks (block_m) the library takes: the walk-through's BLOCK_M candidates (section 7.1).
 constexpr int kBlockLadder[] = {16, 32, 64, 96, 128, 192};
@@ -81,7 +89,7 @@ inline PlanLayout plan_layout(const moe_shape& s) {
     L.block_expert = take((size_t)L.max_blocks * 4);
     L.slack = take((size_t)L.max_blocks * 4);
     L.pull_order = take((size_t)s.num_tokens * 4);
-    L.groups = (s.num_tokens + kRouteTokensPerGroup - 1) / kRouteTokensPerGroup;
+    L.groups = (s.num_tokens + route_group_tokens(s.num_tokens) - 1) / route_group_tokens(s.num_tokens);
     L.group_counts = take((size_t)L.groups * s.num_experts * 2 * 4);  // hit and pull counts per group
     // GEMM tile lists: tile = (expert, M-tile, N-tile), M-tile by M-tile, all N-tiles of each
     L.bmg = gemm_bm(s.block_m);

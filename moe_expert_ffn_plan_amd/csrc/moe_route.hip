@@ -22,8 +22,9 @@
 // lies in the range of its smallest expert, and tokens of one expert are in
 // ascending t there).  The scans use DPP lane moves, not LDS shuffles.
 //
-// Larger inputs spread over many CUs in groups of kRouteTokensPerGroup
-// tokens: route_count_kernel (per group: hit counts per expert and pull
+// Larger inputs spread over many CUs in groups of route_group_tokens(T)
+// tokens (64, or up to 256 so that there are at most 256 groups where
+// possible; one token per lane of a group's four waves): route_count_kernel (per group: hit counts per expert and pull
 // counts per smallest expert), then route_scatter_scan_kernel (per group:
 // the bases of its group from the counts of all groups, the counts, padded
 // offsets, block tables and tile lists, and the same stable ballot-match
@@ -344,7 +345,6 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
 // ---------------------------------------------------------------- multi-group path
 constexpr int kGThreads = 256;
 constexpr int kGWaves = kGThreads / 64;
-constexpr int kWaveTokens = kRouteTokensPerGroup / kGWaves;  // contiguous tokens per wave
 
 // Loads the group's top-k ids once (coalesced, 8 loads in flight per thread) as local expert
 // ids, -1 when not local, into LDS `le` [tokens * k].
@@ -398,15 +398,15 @@ __device__ __forceinline__ int smallest_in(const int16_t* le, int t_local, int k
 
 // group_counts: [groups][E] hit counts, then [groups][E] pull counts.
 __global__ __launch_bounds__(kGThreads) void route_count_kernel(const int64_t* __restrict__ ids, int T, int k, int E,
-                                                               int expert_begin, int groups,
+                                                               int expert_begin, int groups, int tpg,
                                                                int32_t* __restrict__ gcounts) {
     extern __shared__ int32_t lds[];
     int32_t* ch = lds;                                          // [E]
     int32_t* cp = lds + E;                                      // [E]
-    int16_t* le = reinterpret_cast<int16_t*>(lds + 2 * E);      // [kRouteTokensPerGroup * k]
+    int16_t* le = reinterpret_cast<int16_t*>(lds + 2 * E);      // [tpg * k]
     const int tid = threadIdx.x, g = blockIdx.x;
     for (int i = tid; i < 2 * E; i += kGThreads) lds[i] = 0;
-    const int t0 = g * kRouteTokensPerGroup, t1 = min(T, t0 + kRouteTokensPerGroup);
+    const int t0 = g * tpg, t1 = min(T, t0 + tpg);
     load_group_experts(ids, (int64_t)t0 * k, (int64_t)t1 * k, k, expert_begin, E, le);
     lds_barrier();
     const int nh = (t1 - t0) * k;
@@ -526,20 +526,21 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(int E, int bm, int
 }
 
 __global__ __launch_bounds__(kGThreads) void route_scatter_kernel(const int64_t* __restrict__ ids, int T, int k, int E,
-                                                                 int expert_begin, int groups,
+                                                                 int expert_begin, int groups, int tpg,
                                                                  const int32_t* __restrict__ gcounts, PlanPtrs p) {
     extern __shared__ int32_t lds[];
     int32_t* wh = lds;                                           // [kGWaves][E] running hit rows
     int32_t* wp = lds + kGWaves * E;                             // [kGWaves][E] running pull positions
-    int16_t* le = reinterpret_cast<int16_t*>(lds + 2 * kGWaves * E);  // [kRouteTokensPerGroup * k]
+    int16_t* le = reinterpret_cast<int16_t*>(lds + 2 * kGWaves * E);  // [tpg * k]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = blockIdx.x;
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     for (int i = tid; i < 2 * kGWaves * E; i += kGThreads) lds[i] = 0;
-    const int tg0 = g * kRouteTokensPerGroup, tg1 = min(T, tg0 + kRouteTokensPerGroup);
+    const int tg0 = g * tpg, tg1 = min(T, tg0 + tpg);
     load_group_experts(ids, (int64_t)tg0 * k, (int64_t)tg1 * k, k, expert_begin, E, le);
     __syncthreads();
-    const int t0 = min(tg1, tg0 + w * kWaveTokens);  // this wave's tokens [t0, t1)
-    const int t1 = min(tg1, t0 + kWaveTokens);
+    const int wt = tpg / kGWaves;                  // tokens per wave, at most 64
+    const int t0 = min(tg1, tg0 + w * wt);  // this wave's tokens [t0, t1)
+    const int t1 = min(tg1, t0 + wt);
     const int l0 = (t0 - tg0) * k, l1 = (t1 - tg0) * k;  // and hits (group-local)
     for (int i = l0 + lane; i < l1; i += 64)
         if (le[i] >= 0) atomicAdd(&wh[w * E + le[i]], 1);
@@ -595,8 +596,8 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_kernel(const int64_t*
 constexpr int kFusedScanMaxWords = 65536;  // groups * E up to this takes the two-kernel path
 
 __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int64_t* __restrict__ ids, int T, int k,
-                                                                      int E, int expert_begin, int groups, int bm,
-                                                                      const int32_t* __restrict__ gcounts,
+                                                                      int E, int expert_begin, int groups, int tpg,
+                                                                      int bm, const int32_t* __restrict__ gcounts,
                                                                       PlanPtrs p) {
     extern __shared__ int32_t lds[];
     int32_t* wh = lds;                      // [kGWaves][E] running hit rows
@@ -609,11 +610,11 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int
     int32_t* scratch = gp + E;              // [192]
     int32_t* tb = scratch + 192;            // [E+1] M-tile bases
     int32_t* part = tb + E + 1;             // [4][kGThreads] partial sums of the group-count scan
-    int16_t* le = reinterpret_cast<int16_t*>(part + 4 * kGThreads);  // [kRouteTokensPerGroup * k]
+    int16_t* le = reinterpret_cast<int16_t*>(part + 4 * kGThreads);  // [tpg * k]
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = blockIdx.x;
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     for (int i = tid; i < 2 * kGWaves * E; i += kGThreads) lds[i] = 0;
-    const int tg0 = g * kRouteTokensPerGroup, tg1 = min(T, tg0 + kRouteTokensPerGroup);
+    const int tg0 = g * tpg, tg1 = min(T, tg0 + tpg);
     const int nh = (tg1 - tg0) * k;
     int64_t idv[8];
     fetch_ids(ids, (int64_t)tg0 * k, nh, idv);  // in flight during the group-count loads below
@@ -703,8 +704,9 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int
     lds_barrier();
 
     // ---- this group's per-wave bases, then the stable scatter (as in route_scatter_kernel)
-    const int t0 = min(tg1, tg0 + w * kWaveTokens);
-    const int t1 = min(tg1, t0 + kWaveTokens);
+    const int wt = tpg / kGWaves;  // tokens per wave, at most 64
+    const int t0 = min(tg1, tg0 + w * wt);
+    const int t1 = min(tg1, t0 + wt);
     const int l0 = (t0 - tg0) * k, l1 = (t1 - tg0) * k;
     for (int i = l0 + lane; i < l1; i += 64)
         if (le[i] >= 0) atomicAdd(&wh[w * E + le[i]], 1);
@@ -778,20 +780,21 @@ hipError_t launch_route(const moe_shape& s, const int64_t* topk_idx, const PlanP
                            s.expert_begin, s.block_m, p);
         return hipGetLastError();
     }
-    const int groups = (s.num_tokens + kRouteTokensPerGroup - 1) / kRouteTokensPerGroup;
-    const size_t le_bytes = (size_t)kRouteTokensPerGroup * s.topk * 2;
+    const int tpg = route_group_tokens(s.num_tokens);
+    const int groups = (s.num_tokens + tpg - 1) / tpg;
+    const size_t le_bytes = (size_t)tpg * s.topk * 2;
     hipLaunchKernelGGL(route_count_kernel, dim3(groups), dim3(kGThreads), (size_t)2 * E * 4 + le_bytes, stream,
-                       topk_idx, s.num_tokens, s.topk, E, s.expert_begin, groups, p.group_counts);
+                       topk_idx, s.num_tokens, s.topk, E, s.expert_begin, groups, tpg, p.group_counts);
     if ((int64_t)groups * E <= kFusedScanMaxWords) {
         const size_t lds = (size_t)(2 * kGWaves * E + 6 * E + 3 + 192 + 4 * kGThreads) * 4 + le_bytes;
         hipLaunchKernelGGL(route_scatter_scan_kernel, dim3(groups), dim3(kGThreads), lds, stream, topk_idx,
-                           s.num_tokens, s.topk, E, s.expert_begin, groups, s.block_m, p.group_counts, p);
+                           s.num_tokens, s.topk, E, s.expert_begin, groups, tpg, s.block_m, p.group_counts, p);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kThreads), (size_t)(5 * E + 3 + 64 + kScanChunkWords) * 4,
                        stream, E, s.block_m, groups, p.group_counts, p);
     hipLaunchKernelGGL(route_scatter_kernel, dim3(groups), dim3(kGThreads), (size_t)2 * kGWaves * E * 4 + le_bytes,
-                       stream, topk_idx, s.num_tokens, s.topk, E, s.expert_begin, groups, p.group_counts, p);
+                       stream, topk_idx, s.num_tokens, s.topk, E, s.expert_begin, groups, tpg, p.group_counts, p);
     return hipGetLastError();
 }
 

@@ -76,10 +76,13 @@ def test_plan_edge_cases(gpu, case):
     assert_plan_equal(g, plan_ref(ids, E, begin, bm))
 
 
-@pytest.mark.parametrize("T,k,E", [(4096, 8, 64), (4097, 8, 64), (32768, 1, 7), (32769, 1, 7), (5000, 8, 512)])
+@pytest.mark.parametrize("T,k,E", [(4096, 8, 64), (4097, 8, 64), (32768, 1, 7), (32769, 1, 7), (5000, 8, 512),
+                                   (16384, 8, 32), (16385, 6, 48), (32769, 2, 48), (70000, 1, 300), (33000, 64, 16)])
 def test_plan_path_boundary(gpu, T, k, E):
     """Inputs just below and above the one-workgroup limit (32768 hits) take different kernels;
-    both must give the oracle's tables."""
+    both must give the oracle's tables.  Past 16384 tokens the groups grow from 64 to 128 tokens,
+    past 32768 to 256 (16385 and 32769 tokens: a last group of one token; 70000 tokens of 300
+    experts: 256-token groups with the separate scan; top-64: the largest group LDS table)."""
     rng = np.random.default_rng(T * 31 + k)
     ids = rng.integers(-2, E + 3, size=(T, k))
     print(f"plan path boundary: T={T} k={k} E={E} hits={T * k}", flush=True)
