@@ -359,14 +359,16 @@ def main() -> int:
     tflops = useful / (ms * 1e-3) / 1e12
     # GEMM M-tile: 128 rows (several routing blocks of one expert) from block_m 32 up, else one block
     bmg = 128 if w.block_m >= 32 else w.block_m
-    partial = "true" if w.block_m < bmg else "false"
+    # tile variant: 0 = M-tile of one routing block, 1 = several blocks of fewer rows, 2 = blocks of more
+    tv = 0 if w.block_m == bmg else (1 if w.block_m < bmg else 2)
+    epi = 0  # the fast SiLU epilogue without a clamp (the bench's default)
     if fused:
         k_flops = useful
-        kname = f"Linear1 + Linear2 in one launch (gemm_fused_kernel<{bmg}, {partial}, 0>)"
+        kname = f"Linear1 + Linear2 in one launch (gemm_fused_kernel<{bmg}, {tv}, {epi}>)"
     else:
         k_flops = 2.0 * n_valid * 2 * I * H
-        kname = "Linear1 grouped GEMM (%s<%d, true, %s, 0>)" % (
-            "gemm_pp_kernel" if (2 * I) % 512 == 0 else "gemm4_kernel", bmg, partial)
+        kname = "Linear1 grouped GEMM (%s<%d, true, %d, %d>)" % (
+            "gemm_pp_kernel" if (2 * I) % 512 == 0 else "gemm4_kernel", bmg, tv, epi)
     k_bytes = kernel_bytes(w, fused, n_valid, touched, hit_tokens)
     # whole step, compulsory: touched weights and scales, x and x_sf of tokens with a local hit, the
     # top-k ids and weights, y
