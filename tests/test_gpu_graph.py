@@ -150,3 +150,60 @@ def test_graphs_share_workspace(gpu, fill):
         want = expect(order)
         for li in range(2):
             assert torch.equal(got[li], want[li].view(torch.int16)), f"step {rep} ({kind}{order}) layer {li} differs"
+
+
+@pytest.mark.parametrize("name", ["skewed", "tp_slice"])
+def test_bench_graph_segments_full_size(gpu, name):
+    """The launch configuration bench.py times, at full size: each step recorded as three graphs (the
+    calls before the dominant GEMM launch, that launch, the calls after it) on a side stream, the
+    graphs of two steps with different weights replayed in turn on one workspace, each output equal
+    bit for bit to an eager moe_forward (the path compared with the oracle at full size) on the same
+    inputs and weights."""
+    w = inputs.WORKLOADS[name]
+    s = B.shape_of(w)
+    fused = B.forward_uses_expert_ffn(s) and B.expert_ffn_is_fused(s)
+    print(f"bench graph segments: {name} full size, one launch={fused}", flush=True)
+    d = {k: v.to(gpu) for k, v in inputs.make_inputs(w, device=gpu).items()}
+    layers = [B.prepare_all(s, d)]
+    lw = {k: v.to(gpu) for k, v in inputs.make_weights(w, device=gpu, weight_seed=w.weight_seed + 1000).items()}
+    layers.append(B.prepare_all(s, lw))
+    del lw
+    ws = torch.full((B.forward_workspace_bytes(s),), 0x5A, dtype=torch.uint8, device=gpu)
+    plan_ws = torch.empty(B.plan_workspace_bytes(s), dtype=torch.uint8, device=gpu)
+    y = torch.empty(w.num_tokens, w.hidden, dtype=torch.bfloat16, device=gpu)
+
+    def segments(wt):
+        pre = [lambda st: B.plan(s, d["topk_idx"], plan_ws, st)]
+        if fused:
+            dom = lambda st: B.expert_ffn(s, d["x"], d["x_sf"], d["topk_w"], wt["w1"], wt["w1_sf"], wt["w2"],  # noqa
+                                          wt["w2_sf"], plan_ws, ws, st)
+            post = [lambda st: B.combine(s, plan_ws, ws, y, st)]
+        else:
+            dom = lambda st: B.linear1(s, d["x"], d["x_sf"], d["topk_w"], wt["w1"], wt["w1_sf"], plan_ws, ws, st)  # noqa
+            post = [lambda st: B.linear2(s, wt["w2"], wt["w2_sf"], plan_ws, ws, st),
+                    lambda st: B.combine(s, plan_ws, ws, y, st)]
+        return [pre, [dom], post]
+
+    side = torch.cuda.Stream()
+    steps = []
+    for wt in layers:
+        graphs = []
+        for part in segments(wt):
+            side.wait_stream(torch.cuda.current_stream())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for call in part:
+                    call(torch.cuda.current_stream())
+            graphs.append(g)
+        steps.append(graphs)
+    torch.cuda.synchronize()
+    want = []
+    for wt in layers:
+        want.append(_eager(s, {**d, **wt}, gpu).view(torch.int16).clone())
+    status = B.forward_view(s, ws)["sync_status"]
+    for rep, li in enumerate((0, 1, 1, 0)):
+        for g in steps[li]:
+            g.replay()
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, f"{name}: replay {rep}: a GEMM launch gave up waiting"
+        assert torch.equal(y.view(torch.int16), want[li]), f"{name}: replay {rep} (weights {li}) differs from eager"
