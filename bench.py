@@ -15,11 +15,12 @@ moe_expert_ffn, both GEMMs in one persistent launch, or moe_linear1 and
 moe_linear2, as moe_gemm_launches reports; moe_combine); they are issued one by one so HIP
 events on that stream can bracket the dominant GEMM launch inside the timed
 steps (the roofline's achieved rate).  --staged and --expert-ffn force one
-schedule or the other.  By default every timed step is recorded as three HIP
-graphs (the calls before the dominant GEMM launch, that launch, the calls
-after it) and the timed loop replays them, recording the events around the
-dominant launch between the replays; --launch stream issues the calls one by
-one instead.  Three copies of the
+schedule or the other.  In the two-launch schedule every timed step is
+recorded as three HIP graphs (the calls before the dominant GEMM launch, that
+launch, the calls after it) and the timed loop replays them, recording the
+events around the dominant launch between the replays; the single-launch
+schedule issues the calls one by one on the stream (--launch graph or stream
+forces either).  Three copies of the
 expert weights are rotated between steps so they stream from HBM rather than
 the 256 MB Infinity Cache.  The default warmup (50 steps) lets the clocks
 settle; the first steps after idle run ~15% slower.
@@ -183,10 +184,11 @@ def main() -> int:
                     help="run Linear1 and Linear2 through moe_expert_ffn (one launch) wherever it is supported")
     ap.add_argument("--host-inputs", action="store_true",
                     help="draw the synthetic inputs on the CPU and copy them (fewer torch GPU kernels, for profilers)")
-    ap.add_argument("--launch", choices=("graph", "stream"), default="graph",
-                    help="graph (default): every timed step recorded as HIP graphs (the calls before the dominant "
-                         "GEMM launch, that launch, the calls after it) and timed as their replays; stream: the "
-                         "library calls issued on the stream step by step")
+    ap.add_argument("--launch", choices=("auto", "graph", "stream"), default="auto",
+                    help="graph: every timed step recorded as HIP graphs (the calls before the dominant GEMM "
+                         "launch, that launch, the calls after it) and timed as their replays; stream: the library "
+                         "calls issued on the stream step by step; auto (default): graph for the two-launch "
+                         "schedule, stream for the single launch")
     ap.add_argument("--block-m", type=int, default=0,
                     help="routing block rows to use instead of the workload's own (16, 32, 64 or 128)")
     ap.add_argument("--tokens", type=int, default=0,
@@ -244,6 +246,9 @@ def main() -> int:
     fused = B.forward_uses_expert_ffn(s) and B.expert_ffn_is_fused(s) and not args.staged
     if args.expert_ffn:
         fused = B.expert_ffn_is_fused(s)
+    # graph replay saves ~16 us per kernel boundary on the millisecond steps of the two-launch schedule;
+    # on the sub-millisecond single-launch steps its three graph launches cost more than that (measured)
+    launch = args.launch if args.launch != "auto" else ("stream" if fused else "graph")
     stages = ["plan", "expert_ffn", "combine"] if fused else ["plan", "linear1", "linear2", "combine"]
 
     def calls(i, staged):
@@ -298,7 +303,7 @@ def main() -> int:
 
     # timed steps: wall time; HIP events bracket only the dominant GEMM launch (same stream)
     k_evs = [[dev_ev.new() for _ in range(2)] for _ in range(args.steps)]
-    if args.launch == "graph":
+    if launch == "graph":
         # every timed step as three recorded graphs (the calls before the dominant GEMM launch, that
         # launch, the calls after it; the weight copies in turn): the events around the dominant launch
         # are recorded between the replays, on the stream they replay on.  Each graph is replayed once
@@ -388,7 +393,7 @@ def main() -> int:
            "config": {"workload": w.name, "tokens": w.num_tokens, "hidden": H, "intermediate": I,
                       "local_experts": w.num_experts, "topk": w.topk, "block_m": w.block_m,
                       "valid_rows": n_valid, "padded_rows": r_pad, "weight_copies": args.weight_copies,
-                      "launch": args.launch},
+                      "launch": launch},
            "tokens_per_s": round(w.num_tokens / (ms * 1e-3), 1),
            "pct_of_mfma_peak": round(100 * tflops / PEAK_MFMA_TFLOPS, 2),
            "pct_of_hbm_peak": round(100 * step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
