@@ -369,7 +369,10 @@ def main() -> int:
     epi = 0  # the fast SiLU epilogue without a clamp (the bench's default)
     if fused:
         k_flops = useful
-        kname = f"Linear1 + Linear2 in one launch (gemm_fused_kernel<{bmg}, {tv}, {epi}>)"
+        # the events bracket moe_expert_ffn: its one-thread prepare kernel (launch counter, status word)
+        # and the single launch
+        kname = (f"Linear1 + Linear2 in one launch (fused_prepare_kernel + gemm_fused_kernel<{bmg}, {tv}, "
+                 f"{epi}>)")
     else:
         k_flops = 2.0 * n_valid * 2 * I * H
         kname = "Linear1 grouped GEMM (%s<%d, true, %d, %d>)" % (
