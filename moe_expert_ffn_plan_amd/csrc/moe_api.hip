@@ -235,9 +235,14 @@ int moe_linear2(const moe_shape* shape, const uint8_t* w2, const uint8_t* w2_sf,
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-int moe_expert_ffn(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
-                   const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2, const uint8_t* w2_sf,
-                   const void* plan_ws, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// moe_expert_ffn; prepared: the routing kernels enqueued just before did the single launch's prepare
+// work (moe_forward building its plan inside ws), so no prepare kernel is enqueued.
+int expert_ffn_call(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
+                    const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2, const uint8_t* w2_sf,
+                    const void* plan_ws, void* ws, size_t ws_bytes, void* stream, bool prepared) {
     int st = check_weight_shape(shape);
     if (st != MOE_OK) return st;
     if (shape->num_tokens == 0) return MOE_OK;
@@ -255,8 +260,17 @@ int moe_expert_ffn(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf
         g, x, x_sf, topk_w, w1, w1_sf, reinterpret_cast<uint8_t*>(base + F.h_q),
         reinterpret_cast<uint8_t*>(base + F.h_sf), w2, w2_sf, reinterpret_cast<uint16_t*>(base + F.yslot),
         reinterpret_cast<uint32_t*>(base + F.flags), reinterpret_cast<uint32_t*>(base + F.status),
-        reinterpret_cast<uint32_t*>(base + F.epoch), static_cast<hipStream_t>(stream));
+        reinterpret_cast<uint32_t*>(base + F.epoch), static_cast<hipStream_t>(stream), prepared);
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+}  // namespace
+
+extern "C" {
+
+int moe_expert_ffn(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
+                   const uint8_t* w1, const uint8_t* w1_sf, const uint8_t* w2, const uint8_t* w2_sf,
+                   const void* plan_ws, void* ws, size_t ws_bytes, void* stream) {
+    return expert_ffn_call(shape, x, x_sf, topk_w, w1, w1_sf, w2, w2_sf, plan_ws, ws, ws_bytes, stream, false);
 }
 
 int moe_combine(const moe_shape* shape, const void* plan_ws, const void* ws, size_t ws_bytes, uint16_t* y,
@@ -294,13 +308,19 @@ int moe_forward(const moe_shape* shape, const uint8_t* x, const uint8_t* x_sf, c
     if ((st = check_arch_current()) != MOE_OK) return st;
     char* base = static_cast<char*>(ws);
     const void* plan = plan_ws ? plan_ws : static_cast<const void*>(base + F.plan_base);
+    const bool one_launch = forward_one_launch(*shape, cu_count());
     if (!plan_ws) {
-        const hipError_t e = launch_route(*shape, topk_idx, plan_ptrs(F.plan, base + F.plan_base),
-                                          static_cast<hipStream_t>(stream));
+        PlanPtrs pp = plan_ptrs(F.plan, base + F.plan_base);
+        if (one_launch) {  // the routing kernels also do the single launch's prepare work
+            pp.epoch_word = reinterpret_cast<uint32_t*>(base + F.epoch);
+            pp.status = reinterpret_cast<uint32_t*>(base + F.status);
+        }
+        const hipError_t e = launch_route(*shape, topk_idx, pp, static_cast<hipStream_t>(stream));
         if (e != hipSuccess) return MOE_ERR_HIP;
     }
-    if (forward_one_launch(*shape, cu_count())) {
-        if ((st = moe_expert_ffn(shape, x, x_sf, topk_w, w1, w1_sf, w2, w2_sf, plan, ws, ws_bytes, stream)) != MOE_OK)
+    if (one_launch) {
+        if ((st = expert_ffn_call(shape, x, x_sf, topk_w, w1, w1_sf, w2, w2_sf, plan, ws, ws_bytes, stream,
+                                  !plan_ws)) != MOE_OK)
             return st;
     } else {
         if ((st = moe_linear1(shape, x, x_sf, topk_w, w1, w1_sf, plan, ws, ws_bytes, stream)) != MOE_OK) return st;

@@ -1235,7 +1235,7 @@ bool forward_one_launch(const moe_shape& s, int cus) {
 hipError_t launch_expert_ffn(const GemmProblem& p, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
                              const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf,
                              const uint8_t* w2, const uint8_t* w2_sf, uint16_t* yslot, uint32_t* flags,
-                             uint32_t* status, uint32_t* epoch_word, hipStream_t stream) {
+                             uint32_t* status, uint32_t* epoch_word, hipStream_t stream, bool prepared) {
     FusedArgs fa{};
     fa.g1 = linear1_args(p, x, x_sf, topk_w, w1, w1_sf, h_q, h_sf, status);
     fa.g2 = linear2_args(p, h_q, h_sf, w2, w2_sf, yslot);
@@ -1254,10 +1254,13 @@ hipError_t launch_expert_ffn(const GemmProblem& p, const uint8_t* x, const uint8
     const dim3 grid((unsigned)persistent_grid(tiles)), block(512);
     const int bm = p.shape->block_m, bmg = gemm_bm(bm);
     const int epi = epi_of(fa.g1);
-    // advance the launch counter (eager or recorded alike), so that this launch's flag value is new
-    hipLaunchKernelGGL(fused_prepare_kernel, dim3(1), dim3(64), 0, stream, epoch_word, status);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // advance the launch counter (eager or recorded alike), so that this launch's flag value is new, and
+    // clear the status word: here, or done by the routing kernels just enqueued
+    if (!prepared) {
+        hipLaunchKernelGGL(fused_prepare_kernel, dim3(1), dim3(64), 0, stream, epoch_word, status);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     if (bmg == 16) launch_fused<16, kTileFull>(epi, grid, block, stream, fa);
     else if (bm == 128) launch_fused<128, kTileFull>(epi, grid, block, stream, fa);
     else if (bm < 128) launch_fused<128, kTileShortStream>(epi, grid, block, stream, fa);

@@ -130,14 +130,23 @@ struct PlanPtrs {
     int32_t *scalars, *counts, *offsets, *slot, *row_token, *row_topk, *block_expert, *slack, *pull_order,
         *group_counts, *tiles1, *tiles2;
     int nt1, nt2, bmg;
+    // Optional: when set, the routing kernels also do the single launch's prepare work (advance the
+    // workspace's launch counter, clear its status word), so that a single launch enqueued right after
+    // them needs no prepare kernel of its own (moe_forward building its plan inside the workspace).
+    uint32_t* epoch_word = nullptr;
+    uint32_t* status = nullptr;
 };
 
 inline PlanPtrs plan_ptrs(const PlanLayout& L, void* base) {
     char* b = static_cast<char*>(base);
     auto at = [&](size_t off) { return reinterpret_cast<int32_t*>(b + off); };
-    return PlanPtrs{at(L.scalars),   at(L.counts),     at(L.offsets),      at(L.slot),   at(L.row_token),
-                    at(L.row_topk),  at(L.block_expert), at(L.slack),      at(L.pull_order), at(L.group_counts),
-                    at(L.tiles1),    at(L.tiles2),     L.nt1,              L.nt2,        L.bmg};
+    PlanPtrs p;
+    p.scalars = at(L.scalars); p.counts = at(L.counts); p.offsets = at(L.offsets); p.slot = at(L.slot);
+    p.row_token = at(L.row_token); p.row_topk = at(L.row_topk); p.block_expert = at(L.block_expert);
+    p.slack = at(L.slack); p.pull_order = at(L.pull_order); p.group_counts = at(L.group_counts);
+    p.tiles1 = at(L.tiles1); p.tiles2 = at(L.tiles2);
+    p.nt1 = L.nt1; p.nt2 = L.nt2; p.bmg = L.bmg;
+    return p;
 }
 
 // ---- launchers (each enqueues on `stream` and returns the launch status) ----
@@ -171,10 +180,12 @@ bool fused_supported(const moe_shape& s);
 constexpr int kOneLaunchTilesPerCu = 16;
 bool forward_one_launch(const moe_shape& s, int cus);
 int cu_count();  // compute units of the current device (256 if it cannot be queried)
+// prepared: the kernels enqueued just before this call did the prepare work already (PlanPtrs'
+// epoch_word and status), so no prepare kernel is enqueued.
 hipError_t launch_expert_ffn(const GemmProblem& g, const uint8_t* x, const uint8_t* x_sf, const float* topk_w,
                              const uint8_t* w1, const uint8_t* w1_sf, uint8_t* h_q, uint8_t* h_sf,
                              const uint8_t* w2, const uint8_t* w2_sf, uint16_t* yslot, uint32_t* flags,
-                             uint32_t* status, uint32_t* epoch_word, hipStream_t stream);
+                             uint32_t* status, uint32_t* epoch_word, hipStream_t stream, bool prepared = false);
 hipError_t launch_tile_weights(int which, int N, int K, int E, const uint8_t* w, const uint8_t* w_sf,
                                uint8_t* w_out, uint8_t* sf_out, hipStream_t stream);
 // status: the forward's status word; when it is non-zero (a single-launch GEMM gave up waiting) every

@@ -47,6 +47,16 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// The single launch's prepare work, when the plan asks for it (PlanPtrs' epoch_word and status): one
+// thread advances the launch counter and clears the status word, as the fused prepare kernel does.
+__device__ __forceinline__ void plan_prepare(const PlanPtrs& p) {
+    if (p.epoch_word && blockIdx.x == 0 && threadIdx.x == 0) {
+        const uint32_t v = __hip_atomic_load(p.epoch_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.epoch_word, v + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.status, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // Wave-level inclusive scans with DPP lane moves (a few cycles each; a __shfl_up goes through the LDS
 // crossbar at LDS latency).  Lanes whose source lies outside the row read 0.
 template <int CTRL, int ROWS = 0xF>
@@ -211,6 +221,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     const int64_t begin = expert_begin;
     const int nh = T * k;
+    plan_prepare(p);
 
     // ---- pass 0: ids -> local experts in LDS (8 loads in flight per thread), counters cleared
     for (int base = 0; base < nh; base += 8 * kThreads) {
@@ -430,6 +441,7 @@ constexpr int kScanChunkWords = 8192;
 
 __global__ __launch_bounds__(kThreads) void route_scan_kernel(int E, int bm, int groups, int32_t* __restrict__ gcounts,
                                                              PlanPtrs p) {
+    plan_prepare(p);
     extern __shared__ int32_t lds[];
     int32_t* soff = lds;            // [E+1] padded offsets
     int32_t* scnt = soff + E + 1;   // [E] hit counts
@@ -599,6 +611,7 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int
                                                                       int E, int expert_begin, int groups, int tpg,
                                                                       int bm, const int32_t* __restrict__ gcounts,
                                                                       PlanPtrs p) {
+    plan_prepare(p);
     extern __shared__ int32_t lds[];
     int32_t* wh = lds;                      // [kGWaves][E] running hit rows
     int32_t* wp = wh + kGWaves * E;         // [kGWaves][E] running pull positions

@@ -39,11 +39,15 @@ def _eager(s, d, dev):
     return y
 
 
+@pytest.mark.parametrize("internal_plan", [False, True])
 @pytest.mark.parametrize("name", list(CASES))
-def test_forward_graph_replays(gpu, name):
+def test_forward_graph_replays(gpu, name, internal_plan):
+    """internal_plan: moe_forward builds the plan inside its workspace, and its routing kernels also
+    advance the launch counter that the single launch's flags take their value from."""
     w = CASES[name]
     s = B.shape_of(w)
-    print(f"graph replay: {name} T={w.num_tokens} bm={w.block_m} launches={B.gemm_launches(s)}", flush=True)
+    print(f"graph replay: {name} T={w.num_tokens} bm={w.block_m} launches={B.gemm_launches(s)} "
+          f"internal plan={internal_plan}", flush=True)
     weights = {k: v.to(gpu) for k, v in inputs.make_weights(w, device="cpu").items()}
     weights.update(B.prepare_all(s, weights))
 
@@ -60,9 +64,10 @@ def test_forward_graph_replays(gpu, name):
     status.zero_()
 
     def run():
-        B.plan(s, static["topk_idx"], plan_ws)
+        if not internal_plan:
+            B.plan(s, static["topk_idx"], plan_ws)
         B.forward(s, static["x"], static["x_sf"], static["topk_idx"], static["topk_w"], static["w1"],
-                  static["w1_sf"], static["w2"], static["w2_sf"], y, ws, plan_ws=plan_ws)
+                  static["w1_sf"], static["w2"], static["w2_sf"], y, ws, plan_ws=None if internal_plan else plan_ws)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -83,6 +88,10 @@ def test_forward_graph_replays(gpu, name):
         torch.cuda.synchronize()
         want = _eager(s, new, gpu)  # eager work between replays
         assert torch.equal(y.view(torch.int16), want.view(torch.int16)), f"{name}: replay {rep} differs from eager"
+        if internal_plan:  # an eager forward on the captured workspace between replays
+            run()
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), want.view(torch.int16)), f"{name}: eager call {rep} differs"
     assert int(status.item()) == 0, "a Linear2 tile gave up waiting"
 
 
