@@ -182,6 +182,11 @@ def main() -> int:
                     help="run Linear1 and Linear2 as two launches (moe_linear1, moe_linear2) for every shape")
     ap.add_argument("--expert-ffn", action="store_true",
                     help="run Linear1 and Linear2 through moe_expert_ffn (one launch) wherever it is supported")
+    ap.add_argument("--forward", action="store_true",
+                    help="time whole moe_forward calls (the plan built inside the workspace, one call per step); "
+                         "the events then bracket the whole forward and the roofline is the step's")
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="record the events around the dominant launch on every N-th timed step (default 4)")
     ap.add_argument("--host-inputs", action="store_true",
                     help="draw the synthetic inputs on the CPU and copy them (fewer torch GPU kernels, for profilers)")
     ap.add_argument("--launch", choices=("auto", "graph", "stream"), default="auto",
@@ -197,6 +202,9 @@ def main() -> int:
                     help="only run a plain elementwise copy (y = -x, float32) of this many MiB five times: the "
                          "reference kernel for scaling HBM byte counters")
     args = ap.parse_args()
+    if args.event_every < 1:
+        print("bench.py: --event-every must be at least 1", file=sys.stderr)
+        return 2
     if args.gpus != 1:
         print(f"bench.py: this build runs one GPU's share of the MoE layer; --gpus {args.gpus} is not supported "
               f"(only one GPU's share is built: no sharding across GPUs, no collectives)", file=sys.stderr)
@@ -248,23 +256,30 @@ def main() -> int:
         fused = B.expert_ffn_is_fused(s)
     # graph replay saves ~16 us per kernel boundary on the millisecond steps of the two-launch schedule;
     # on the sub-millisecond single-launch steps its three graph launches cost more than that (measured)
-    launch = args.launch if args.launch != "auto" else ("stream" if fused else "graph")
-    stages = ["plan", "expert_ffn", "combine"] if fused else ["plan", "linear1", "linear2", "combine"]
+    launch = args.launch if args.launch != "auto" else ("stream" if fused or args.forward else "graph")
+
+    def bind_calls(wt, staged):
+        """The step's library calls in order, as (stage name, call on a stream), their arguments checked
+        and marshalled once here (binding.Bound), so that the timed loop only enqueues; the dominant GEMM
+        launch is the one named linear1 or expert_ffn."""
+        if args.forward:
+            return [("forward", B.forward(s, d["x"], d["x_sf"], d["topk_idx"], d["topk_w"], wt["w1"], wt["w1_sf"],
+                                          wt["w2"], wt["w2_sf"], y, ws, bind=True))]
+        c = [("plan", B.plan(s, d["topk_idx"], plan_ws, bind=True))]
+        if staged:
+            c.append(("linear1", B.linear1(s, d["x"], d["x_sf"], d["topk_w"], wt["w1"], wt["w1_sf"], plan_ws, ws,
+                                           bind=True)))
+            c.append(("linear2", B.linear2(s, wt["w2"], wt["w2_sf"], plan_ws, ws, bind=True)))
+        else:
+            c.append(("expert_ffn", B.expert_ffn(s, d["x"], d["x_sf"], d["topk_w"], wt["w1"], wt["w1_sf"], wt["w2"],
+                                                 wt["w2_sf"], plan_ws, ws, bind=True)))
+        c.append(("combine", B.combine(s, plan_ws, ws, y, bind=True)))
+        return c
+
+    bound = {(c, staged): bind_calls(weights[c], staged) for c in range(len(weights)) for staged in (False, True)}
 
     def calls(i, staged):
-        """The step's library calls in order, as (stage name, call on a stream); the dominant GEMM launch
-        is the one named linear1 or expert_ffn."""
-        wt = weights[i % len(weights)]
-        c = [("plan", lambda st: B.plan(s, d["topk_idx"], plan_ws, st))]
-        if staged:
-            c.append(("linear1", lambda st: B.linear1(s, d["x"], d["x_sf"], d["topk_w"], wt["w1"], wt["w1_sf"],
-                                                      plan_ws, ws, st)))
-            c.append(("linear2", lambda st: B.linear2(s, wt["w2"], wt["w2_sf"], plan_ws, ws, st)))
-        else:
-            c.append(("expert_ffn", lambda st: B.expert_ffn(s, d["x"], d["x_sf"], d["topk_w"], wt["w1"], wt["w1_sf"],
-                                                            wt["w2"], wt["w2_sf"], plan_ws, ws, st)))
-        c.append(("combine", lambda st: B.combine(s, plan_ws, ws, y, st)))
-        return c
+        return bound[(i % len(weights), staged)]
 
     def step(i, events=None, k_events=None, staged=not fused):
         """One step; events: one per stage boundary; k_events: around the dominant GEMM launch."""
@@ -273,7 +288,7 @@ def main() -> int:
         for j, (name, call) in enumerate(c):
             if events is not None:
                 dev_ev.record(events[j], stream)
-            dominant = k_events is not None and name in ("linear1", "expert_ffn")
+            dominant = k_events is not None and name in ("linear1", "expert_ffn", "forward")
             if dominant:
                 dev_ev.record(k_events[0], stream)
             call(stream)
@@ -285,7 +300,7 @@ def main() -> int:
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    pv = B.plan_view(s, plan_ws)
+    pv = B.plan_view(s, B.forward_view(s, ws)["plan_ws"] if args.forward else plan_ws)
     scal = pv["scalars"].cpu().tolist()
     r_pad, n_valid = scal[0], scal[2]
     touched = int((pv["counts"] > 0).sum().item())  # experts with at least one row
@@ -302,7 +317,9 @@ def main() -> int:
     check_status("warmup")
 
     # timed steps: wall time; HIP events bracket only the dominant GEMM launch (same stream)
-    k_evs = [[dev_ev.new() for _ in range(2)] for _ in range(args.steps)]
+    # events around the dominant launch of every event_every-th timed step (each pair of records costs
+    # the stream a few microseconds, which matters on the 0.1 ms steps)
+    k_evs = [[dev_ev.new() for _ in range(2)] if i % args.event_every == 0 else None for i in range(args.steps)]
     if launch == "graph":
         # every timed step as three recorded graphs (the calls before the dominant GEMM launch, that
         # launch, the calls after it; the weight copies in turn): the events around the dominant launch
@@ -312,28 +329,35 @@ def main() -> int:
         segs = []
         for i in range(args.steps):
             c = calls(i, not fused)
-            k = next(j for j, (name, _) in enumerate(c) if name in ("linear1", "expert_ffn"))
+            k = next(j for j, (name, _) in enumerate(c) if name in ("linear1", "expert_ffn", "forward"))
             parts = []
             for part in (c[:k], c[k:k + 1], c[k + 1:]):
-                side.wait_stream(torch.cuda.current_stream())
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=side):
-                    for _, call in part:
-                        call(torch.cuda.current_stream())
+                g = None
+                if part:  # (the whole-forward call has nothing before or after it)
+                    side.wait_stream(torch.cuda.current_stream())
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=side):
+                        for _, call in part:
+                            call(torch.cuda.current_stream())
                 parts.append(g)
             segs.append(parts)
         torch.cuda.synchronize()
         for parts in segs:
             for g in parts:
-                g.replay()
+                if g is not None:
+                    g.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i, (pre, dom, post) in enumerate(segs):
-            pre.replay()
-            dev_ev.record(k_evs[i][0], stream)
+            if pre is not None:
+                pre.replay()
+            if k_evs[i] is not None:
+                dev_ev.record(k_evs[i][0], stream)
             dom.replay()
-            dev_ev.record(k_evs[i][1], stream)
-            post.replay()
+            if k_evs[i] is not None:
+                dev_ev.record(k_evs[i][1], stream)
+            if post is not None:
+                post.replay()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     else:
@@ -344,12 +368,13 @@ def main() -> int:
         torch.cuda.synchronize()
         t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
-    k_ms = sum(dev_ev.elapsed_ms(e[0], e[1]) for e in k_evs) / args.steps
+    timed_evs = [e for e in k_evs if e is not None]
+    k_ms = sum(dev_ev.elapsed_ms(e[0], e[1]) for e in timed_evs) / len(timed_evs)
     check_status("timed steps")
 
     # untimed breakdown passes: an event between every stage (and the two-launch path for comparison)
     def breakdown(staged):
-        names = ["plan", "linear1", "linear2", "combine"] if staged else stages
+        names = [name for name, _ in calls(0, staged)]
         evs = [[dev_ev.new() for _ in range(len(names) + 1)] for _ in range(args.steps)]
         for i in range(args.steps):
             step(i, evs[i], staged=staged)
@@ -357,7 +382,7 @@ def main() -> int:
         return {name: sum(dev_ev.elapsed_ms(e[j], e[j + 1]) for e in evs) / args.steps
                 for j, name in enumerate(names)}
     kern_ms = breakdown(not fused)
-    staged_ms = breakdown(True) if fused else None
+    staged_ms = breakdown(True) if fused and not args.forward else None
 
     H, I = w.hidden, w.intermediate
     useful = 2.0 * n_valid * 3 * H * I
@@ -382,6 +407,10 @@ def main() -> int:
     # top-k ids and weights, y
     step_bytes = int(touched * 3 * I * H * (1 / 2 + 1 / 32) + hit_tokens * H * (1 + 1 / 32) +
                      w.num_tokens * w.topk * 12 + w.num_tokens * H * 2)
+    if args.forward:  # the events bracket the whole forward: its roofline is the step's
+        k_flops, k_bytes = useful, step_bytes
+        kname = ("whole moe_forward (routing, " + ("single GEMM launch" if fused else "two GEMM launches") +
+                 ", combine)")
     # the roofline that bounds the kernel: the larger of its MFMA time and its HBM time at peak
     if k_bytes / (PEAK_HBM_GBS * 1e9) > k_flops / (PEAK_MFMA_TFLOPS * 1e12):
         achieved, peak, unit, bound = k_bytes / (k_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
@@ -389,14 +418,14 @@ def main() -> int:
         achieved, peak, unit, bound = k_flops / (k_ms * 1e-3) / 1e12, PEAK_MFMA_TFLOPS, "TFLOP/s", "mfma"
     roofline = {"kernel": kname, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "algorithmic_flops": k_flops, "algorithmic_bytes": k_bytes,
-                "traffic": kernel_traffic("expert_ffn" if fused else "linear1", w.name)}
+                "traffic": None if args.forward else kernel_traffic("expert_ffn" if fused else "linear1", w.name)}
     out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "fp8e4m3 x fp4e2m1 (fp32 accumulate)", "data": "synthetic",
            "config": {"workload": w.name, "tokens": w.num_tokens, "hidden": H, "intermediate": I,
                       "local_experts": w.num_experts, "topk": w.topk, "block_m": w.block_m,
                       "valid_rows": n_valid, "padded_rows": r_pad, "weight_copies": args.weight_copies,
-                      "launch": launch},
+                      "launch": launch, "calls": "moe_forward" if args.forward else "stages"},
            "tokens_per_s": round(w.num_tokens / (ms * 1e-3), 1),
            "pct_of_mfma_peak": round(100 * tflops / PEAK_MFMA_TFLOPS, 2),
            "pct_of_hbm_peak": round(100 * step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),

@@ -171,16 +171,39 @@ def status_str(status: int) -> str:
     return lib().moe_status_str(status).decode()
 
 
-def plan(shape: MoeShape, topk_idx: torch.Tensor, plan_ws: torch.Tensor, stream=None) -> None:
+class Bound:
+    """One library call with its arguments checked and marshalled once: calling it with a stream (None:
+    torch's current one) enqueues the call and raises on an error status.  It keeps the shape and the
+    tensors it points at alive.  For loops that issue the same calls many times (the benchmark)."""
+    __slots__ = ("fn", "name", "args", "keep")
+
+    def __init__(self, fn, name, args, keep):
+        self.fn, self.name, self.args, self.keep = fn, name, tuple(args), keep
+
+    def __call__(self, stream=None) -> None:
+        _check(self.name, self.fn(*self.args, _stream(stream)))
+
+
+def _call(name, shape, args, keep, stream, bind):
+    fn = getattr(lib(), name)
+    args = [ctypes.byref(shape)] + list(args)
+    if bind:
+        return Bound(fn, name, args, (shape, keep))
+    _check(name, fn(*args, _stream(stream)))
+    return None
+
+
+def plan(shape: MoeShape, topk_idx: torch.Tensor, plan_ws: torch.Tensor, stream=None, bind=False):
+    """moe_plan; bind=True: return the call as a Bound instead of enqueueing it."""
     dev = plan_ws.device
-    st = lib().moe_plan(ctypes.byref(shape), _ptr(topk_idx, torch.int64, "topk_idx", dev,
-                                                  shape.num_tokens * shape.topk),
-                        _ptr(plan_ws, torch.uint8, "plan_ws"), plan_ws.numel(), _stream(stream))
-    _check("moe_plan", st)
+    args = [_ptr(topk_idx, torch.int64, "topk_idx", dev, shape.num_tokens * shape.topk),
+            _ptr(plan_ws, torch.uint8, "plan_ws"), plan_ws.numel()]
+    return _call("moe_plan", shape, args, (topk_idx, plan_ws), stream, bind)
 
 
 def forward(shape: MoeShape, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y, ws, plan_ws=None,
-            stream=None) -> None:
+            stream=None, bind=False):
+    """moe_forward (plan_ws None: the plan is built inside ws); bind=True: return the call as a Bound."""
     T, H, I, E, k = shape.num_tokens, shape.hidden, shape.intermediate, shape.num_experts, shape.topk
     dev = ws.device
     u8, args = torch.uint8, []
@@ -195,8 +218,9 @@ def forward(shape: MoeShape, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y,
     yv = y.view(torch.int16) if y.dtype == torch.bfloat16 else y
     args.append(_ptr(yv, torch.int16, "y", dev, T * H))
     args.append(_ptr(plan_ws, u8, "plan_ws", dev))
-    st = lib().moe_forward(ctypes.byref(shape), *args, _ptr(ws, u8, "ws"), ws.numel(), _stream(stream))
-    _check("moe_forward", st)
+    args += [_ptr(ws, u8, "ws"), ws.numel()]
+    return _call("moe_forward", shape, args, (x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, y, ws, plan_ws),
+                 stream, bind)
 
 
 NOALLOC_WORKSPACE_BYTES = 32 << 20   # MOE_NOALLOC_WORKSPACE_BYTES
@@ -247,35 +271,33 @@ def untile_row_scales(tiled: torch.Tensor, cap: int, k: int, block_m: int) -> to
     return tiled.view(cap // block_m, k // 128, block_m, 4).permute(0, 2, 1, 3).reshape(cap, k // 32)
 
 
-def linear1(shape: MoeShape, x, x_sf, topk_w, w1, w1_sf, plan_ws, ws, stream=None) -> None:
+def linear1(shape: MoeShape, x, x_sf, topk_w, w1, w1_sf, plan_ws, ws, stream=None, bind=False):
     T, H, I, E, k = shape.num_tokens, shape.hidden, shape.intermediate, shape.num_experts, shape.topk
     dev, u8 = ws.device, torch.uint8
-    st = lib().moe_linear1(ctypes.byref(shape), _ptr(x, u8, "x", dev, T * H), _ptr(x_sf, u8, "x_sf", dev, T * H // 32),
-                           _ptr(topk_w, torch.float32, "topk_w", dev, T * k),
-                           _ptr(w1, u8, "w1", dev, E * 2 * I * H // 2), _ptr(w1_sf, u8, "w1_sf", dev, E * 2 * I * H // 32),
-                           _ptr(plan_ws, u8, "plan_ws", dev), _ptr(ws, u8, "ws"), ws.numel(), _stream(stream))
-    _check("moe_linear1", st)
+    args = [_ptr(x, u8, "x", dev, T * H), _ptr(x_sf, u8, "x_sf", dev, T * H // 32),
+            _ptr(topk_w, torch.float32, "topk_w", dev, T * k),
+            _ptr(w1, u8, "w1", dev, E * 2 * I * H // 2), _ptr(w1_sf, u8, "w1_sf", dev, E * 2 * I * H // 32),
+            _ptr(plan_ws, u8, "plan_ws", dev), _ptr(ws, u8, "ws"), ws.numel()]
+    return _call("moe_linear1", shape, args, (x, x_sf, topk_w, w1, w1_sf, plan_ws, ws), stream, bind)
 
 
-def linear2(shape: MoeShape, w2, w2_sf, plan_ws, ws, stream=None) -> None:
+def linear2(shape: MoeShape, w2, w2_sf, plan_ws, ws, stream=None, bind=False):
     H, I, E = shape.hidden, shape.intermediate, shape.num_experts
     dev, u8 = ws.device, torch.uint8
-    st = lib().moe_linear2(ctypes.byref(shape), _ptr(w2, u8, "w2", dev, E * H * I // 2),
-                           _ptr(w2_sf, u8, "w2_sf", dev, E * H * I // 32), _ptr(plan_ws, u8, "plan_ws", dev),
-                           _ptr(ws, u8, "ws"), ws.numel(), _stream(stream))
-    _check("moe_linear2", st)
+    args = [_ptr(w2, u8, "w2", dev, E * H * I // 2), _ptr(w2_sf, u8, "w2_sf", dev, E * H * I // 32),
+            _ptr(plan_ws, u8, "plan_ws", dev), _ptr(ws, u8, "ws"), ws.numel()]
+    return _call("moe_linear2", shape, args, (w2, w2_sf, plan_ws, ws), stream, bind)
 
 
-def expert_ffn(shape: MoeShape, x, x_sf, topk_w, w1, w1_sf, w2, w2_sf, plan_ws, ws, stream=None) -> None:
+def expert_ffn(shape: MoeShape, x, x_sf, topk_w, w1, w1_sf, w2, w2_sf, plan_ws, ws, stream=None, bind=False):
     T, H, I, E, k = shape.num_tokens, shape.hidden, shape.intermediate, shape.num_experts, shape.topk
     dev, u8 = ws.device, torch.uint8
-    st = lib().moe_expert_ffn(ctypes.byref(shape), _ptr(x, u8, "x", dev, T * H),
-                              _ptr(x_sf, u8, "x_sf", dev, T * H // 32), _ptr(topk_w, torch.float32, "topk_w", dev, T * k),
-                              _ptr(w1, u8, "w1", dev, E * 2 * I * H // 2),
-                              _ptr(w1_sf, u8, "w1_sf", dev, E * 2 * I * H // 32),
-                              _ptr(w2, u8, "w2", dev, E * H * I // 2), _ptr(w2_sf, u8, "w2_sf", dev, E * H * I // 32),
-                              _ptr(plan_ws, u8, "plan_ws", dev), _ptr(ws, u8, "ws"), ws.numel(), _stream(stream))
-    _check("moe_expert_ffn", st)
+    args = [_ptr(x, u8, "x", dev, T * H), _ptr(x_sf, u8, "x_sf", dev, T * H // 32),
+            _ptr(topk_w, torch.float32, "topk_w", dev, T * k),
+            _ptr(w1, u8, "w1", dev, E * 2 * I * H // 2), _ptr(w1_sf, u8, "w1_sf", dev, E * 2 * I * H // 32),
+            _ptr(w2, u8, "w2", dev, E * H * I // 2), _ptr(w2_sf, u8, "w2_sf", dev, E * H * I // 32),
+            _ptr(plan_ws, u8, "plan_ws", dev), _ptr(ws, u8, "ws"), ws.numel()]
+    return _call("moe_expert_ffn", shape, args, (x, x_sf, topk_w, w1, w1_sf, w2, w2_sf, plan_ws, ws), stream, bind)
 
 
 def expert_ffn_is_fused(shape: MoeShape) -> bool:
@@ -288,12 +310,12 @@ def forward_uses_expert_ffn(shape: MoeShape) -> bool:
     return gemm_launches(shape)[1] == 1
 
 
-def combine(shape: MoeShape, plan_ws, ws, y, stream=None) -> None:
+def combine(shape: MoeShape, plan_ws, ws, y, stream=None, bind=False):
     dev = ws.device
     yv = y.view(torch.int16) if y.dtype == torch.bfloat16 else y
-    st = lib().moe_combine(ctypes.byref(shape), _ptr(plan_ws, torch.uint8, "plan_ws", dev), _ptr(ws, torch.uint8, "ws"),
-                           ws.numel(), _ptr(yv, torch.int16, "y", dev, shape.num_tokens * shape.hidden), _stream(stream))
-    _check("moe_combine", st)
+    args = [_ptr(plan_ws, torch.uint8, "plan_ws", dev), _ptr(ws, torch.uint8, "ws"), ws.numel(),
+            _ptr(yv, torch.int16, "y", dev, shape.num_tokens * shape.hidden)]
+    return _call("moe_combine", shape, args, (plan_ws, ws, y), stream, bind)
 
 
 def _slice(base: torch.Tensor, ptr: int, dtype, n: int) -> torch.Tensor:
