@@ -14,7 +14,11 @@ one stream.  The stages are the calls moe_forward makes (moe_plan,
 moe_expert_ffn, both GEMMs in one persistent launch, or moe_linear1 and
 moe_linear2, as moe_gemm_launches reports; moe_combine); they are issued one by one so HIP
 events on that stream can bracket the dominant GEMM launch inside the timed
-steps (the roofline's achieved rate).  --staged and --expert-ffn force one
+steps (the roofline's achieved rate; on every fourth timed step by default,
+--event-every).  Each call's arguments are checked and marshalled once
+before the timed loop (binding.Bound).  --forward times whole moe_forward
+calls instead (the plan built inside the workspace), the events then
+bracketing the whole forward.  --staged and --expert-ffn force one
 schedule or the other.  In the two-launch schedule every timed step is
 recorded as three HIP graphs (the calls before the dominant GEMM launch, that
 launch, the calls after it) and the timed loop replays them, recording the
