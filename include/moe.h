@@ -262,7 +262,8 @@ MOE_API int moe_forward(const moe_shape* shape,
  * top-k weights through the plan's row tables itself) ------------------------
  * moe_forward(plan_ws != NULL) is exactly moe_expert_ffn or moe_linear1 then
  * moe_linear2 (the choice moe_gemm_launches reports), then moe_combine, in
- * this order on one stream; moe_expert_ffn computes what moe_linear1 then
+ * this order on one stream (with plan_ws NULL its routing kernels also do
+ * the single launch's one-thread prepare work, one kernel fewer); moe_expert_ffn computes what moe_linear1 then
  * moe_linear2 compute (bit for bit), in one persistent launch where the
  * shape allows it.  (With few Linear1 tiles per CU the single launch saves a
  * kernel tail and ramp; with many it measured slightly slower.)  They are
