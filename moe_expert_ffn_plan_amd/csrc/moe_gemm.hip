@@ -52,7 +52,7 @@
 //  * Tiles come from a list (expert by expert, M-tile by M-tile, all N-tiles
 //    of each).  An M-tile spans up to 128 rows, several routing blocks of one
 //    expert, so a weight tile is fetched once per 128 rows rather than once
-//    per block; rows past the expert's end are masked.  blockIdx is remapped
+//    per block; rows past the expert's last hit are masked.  blockIdx is remapped
 //    so that each XCD (blockIdx % 8) runs a contiguous range of M-tiles: the
 //    M-tiles sharing a weight tile run together on one XCD and hit its L2.
 #include "moe_internal.h"

@@ -42,9 +42,9 @@ inline bool block_m_supported(int bm) {
 // Tile widths of the two GEMMs: 512 columns when N allows it, else 256.
 inline int gemm_bn(int n) { return n % 512 == 0 ? 512 : 256; }
 // GEMM M-tile: up to 128 rows of one expert once block_m >= 32 (several blocks, part of one, or, with
-// blocks of 96 and 192 rows, spans that cross block boundaries: an expert's padded rows are cut into
-// tiles of 128 from its first row, the last one shorter); for smaller block_m (decode-sized batches, a
-// block or two per expert) the tile is one block.
+// blocks of 96 and 192 rows, spans that cross block boundaries: an expert's rows are cut into tiles of
+// 128 from its first row up to its last hit, the last tile shorter, so no tile holds only padding);
+// for smaller block_m (decode-sized batches, a block or two per expert) the tile is one block.
 inline int gemm_bm(int block_m) { return block_m >= 32 ? 128 : block_m; }
 // Rows past `cap` that the row tables reserve, so a 128-row tile starting at the last block reads
 // allocated memory (the GEMMs mask every row past the tile's valid count).
@@ -68,8 +68,8 @@ inline int64_t capacity_rows(const moe_shape& s) {
     return (raw + s.block_m - 1) / s.block_m * s.block_m;
 }
 
-// Upper bound on the GEMM M-tiles of a routing: expert e has ceil(padded_e / bmg) of them, so at most
-// R_pad / bmg + E over all experts, R_pad <= cap.
+// Upper bound on the GEMM M-tiles of a routing: expert e has ceil(count_e / bmg) <= ceil(padded_e / bmg)
+// of them, so at most R_pad / bmg + E over all experts, R_pad <= cap.
 inline int64_t max_m_tiles(const moe_shape& s) {
     return (capacity_rows(s) + gemm_bm(s.block_m) - 1) / gemm_bm(s.block_m) + s.num_experts;
 }

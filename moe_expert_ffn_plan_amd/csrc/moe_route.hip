@@ -152,14 +152,18 @@ __device__ void wave_prefix(int32_t* cnt, int E, int32_t* totals) {
 }
 
 
-// GEMM tile lists from the padded offsets soff (LDS, E+1).  An M-tile covers up to bmg rows of one
-// expert, cut from the expert's first padded row; expert e has ceil(padded rows / bmg) M-tiles, whose
-// exclusive prefix over experts goes to tb (LDS scratch, E+1), so M-tiles are numbered expert by expert.  For a GEMM with nt
-// N-tiles the list runs M-tile by M-tile, all N-tiles of each: entry l = mt * nt + n = {first row,
-// n << 16 | e, valid rows, mt}.  A range of M-tiles is then a contiguous range of both GEMMs' lists.  Called by every thread of the workgroup; workgroup `part` of `parts` writes the
-// entries l with l / blockDim.x = part mod parts.  scalars[4], [5] = tiles of each GEMM (if `counts`).
-__device__ void write_tile_lists(const int32_t* soff, int E, int32_t* tb, const PlanPtrs& p, int part,
-                                 int parts, bool counts) {
+// GEMM tile lists from the padded offsets soff (LDS, E+1) and the hit counts scnt (LDS, E).  An M-tile
+// covers up to bmg rows of one expert, cut from the expert's first row; expert e has ceil(count / bmg)
+// M-tiles, so a tile that would hold only padding rows is not listed (with blocks of 96 or 192 rows an
+// expert's padding can exceed a 128-row tile), and a tile's row count stops at the expert's last hit.
+// The M-tile counts' exclusive prefix over experts goes to tb (LDS scratch, E+1), so M-tiles are
+// numbered expert by expert.  For a GEMM with nt N-tiles the list runs M-tile by M-tile, all N-tiles
+// of each: entry l = mt * nt + n = {first row, n << 16 | e, valid rows, mt}.  A range of M-tiles is
+// then a contiguous range of both GEMMs' lists.  Called by every thread of the workgroup; workgroup
+// `part` of `parts` writes the entries l with l / blockDim.x = part mod parts.  scalars[4], [5] =
+// tiles of each GEMM (if `counts`).
+__device__ void write_tile_lists(const int32_t* soff, const int32_t* scnt, int E, int32_t* tb, const PlanPtrs& p,
+                                 int part, int parts, bool counts) {
     const int bmg = p.bmg;
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
@@ -167,7 +171,7 @@ __device__ void write_tile_lists(const int32_t* soff, int E, int32_t* tb, const 
         for (int c = 0; c < E; c += 64) {
             const int e = c + lane;
             int v = 0;
-            if (e < E) v = (soff[e + 1] - soff[e] + bmg - 1) / bmg;
+            if (e < E) v = (scnt[e] + bmg - 1) / bmg;
             v = wave_inclusive_scan(v);
             if (e < E) tb[e + 1] = run + v;
             run += __builtin_amdgcn_readlane(v, 63);
@@ -195,7 +199,7 @@ __device__ void write_tile_lists(const int32_t* soff, int E, int32_t* tb, const 
             int32_t* t = tiles + (size_t)kTileWords * l;
             t[0] = m0;
             t[1] = (n << 16) | lo;
-            t[2] = min(bmg, soff[lo + 1] - m0);
+            t[2] = min(bmg, soff[lo] + scnt[lo] - m0);
             t[3] = mt;
         }
     }
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int64_t* __restri
             p.row_topk[q] = -1;
         }
     }
-    write_tile_lists(soff, E, tb, p, 0, 1, true);
+    write_tile_lists(soff, scnt, E, tb, p, 0, 1, true);
     lds_barrier();
 
     // ---- pass 5: pull order = tokens with a hit, by smallest local expert, then t (bases from pass 2)
@@ -534,7 +538,7 @@ __global__ __launch_bounds__(kThreads) void route_scan_kernel(int E, int bm, int
             p.row_topk[q] = -1;
         }
     }
-    write_tile_lists(soff, E, tb, p, 0, 1, true);
+    write_tile_lists(soff, scnt, E, tb, p, 0, 1, true);
 }
 
 __global__ __launch_bounds__(kGThreads) void route_scatter_kernel(const int64_t* __restrict__ ids, int T, int k, int E,
@@ -780,7 +784,7 @@ __global__ __launch_bounds__(kGThreads) void route_scatter_scan_kernel(const int
             p.slack[b] = bm - max(0, min(r + bm, fill_end) - r);
         }
     }
-    write_tile_lists(soff, E, tb, p, g, gridDim.x, g == 0);
+    write_tile_lists(soff, scnt, E, tb, p, g, gridDim.x, g == 0);
 }
 
 }  // namespace
