@@ -583,7 +583,7 @@ __device__ __forceinline__ void load_row_tables(const GemmArgs& g, const TileId&
 }
 
 // Tile variants of the kernels.  kTileFull: every tile is one routing block of BM rows.  The other two
-// cut an expert's padded rows into tiles of up to BM rows that can end early: kTileShortStream for
+// cut an expert's rows into tiles of up to BM rows, the last one ending at its last hit: kTileShortStream for
 // routing blocks below the M-tile (batches with few rows per expert, whose weight tiles serve one or two
 // M-tiles: the weights are streamed with the non-temporal hint, see issue_b_blocks), kTileShortCached for
 // routing blocks above it (192 rows: experts span many M-tiles, which reuse the weight tiles from the
