@@ -210,8 +210,8 @@ def main() -> int:
         print("bench.py: --event-every must be at least 1", file=sys.stderr)
         return 2
     if args.gpus != 1:
-        print(f"bench.py: this build runs one GPU's share of the MoE layer; --gpus {args.gpus} is not supported "
-              f"(only one GPU's share is built: no sharding across GPUs, no collectives)", file=sys.stderr)
+        print(f"bench.py: the library runs one GPU's share of the MoE layer; --gpus {args.gpus} is not supported "
+              f"(no sharding across GPUs, no collectives)", file=sys.stderr)
         return 2
 
     import torch
