@@ -67,7 +67,6 @@ class DeviceEvents:
         self.hip = ctypes.CDLL("libamdhip64.so.7")
         self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-        self.hip.hipEventRecordWithFlags.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.events = []
@@ -81,13 +80,12 @@ class DeviceEvents:
         return e
 
     def record(self, e, stream):
-        """Record on `stream`; while the stream is being captured into a graph, as an event node of the
-        graph (hipEventRecordExternal), so that every replay records it."""
+        """Record on `stream` (not inside a graph capture: the timed graph replays record their events
+        between the replays)."""
         import torch
         if torch.cuda.is_current_stream_capturing():
-            rc = self.hip.hipEventRecordWithFlags(e, ctypes.c_void_p(stream.cuda_stream), 1)
-        else:
-            rc = self.hip.hipEventRecord(e, ctypes.c_void_p(stream.cuda_stream))
+            raise RuntimeError("bench.py: timing events are recorded between graph replays, not captured")
+        rc = self.hip.hipEventRecord(e, ctypes.c_void_p(stream.cuda_stream))
         if rc != 0:
             raise RuntimeError(f"hipEventRecord failed ({rc})")
 
